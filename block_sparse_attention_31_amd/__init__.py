@@ -1,0 +1,21 @@
+"""MI355X-native local-window attention: the local Softmax branch of VDN-H3
+hybrid video attention, as hand-written HIP for gfx950 behind a C ABI.
+
+The HIP library is loaded lazily on the first call (see binding.lib()); there
+is no CPU fallback.
+"""
+
+from .binding import (  # noqa: F401
+    VDN_BF16,
+    VDN_FP8_E4M3,
+    VdnError,
+    lib,
+    local_attn_fwd,
+    vdn_last_error,
+    vdn_local_attn_count_pairs,
+    vdn_local_attn_fwd,
+    vdn_local_attn_kernel_tile_m,
+    vdn_local_attn_key_intervals,
+    vdn_local_attn_num_query_blocks,
+    vdn_local_attn_tile_schedule,
+)

@@ -1,0 +1,225 @@
+// C-ABI front end: argument validation, schedule construction and launch of
+// the forward kernels.  Every check runs before the first HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+
+#include "../../include/vdn_local_attn.h"
+#include "fwd_params.hpp"
+#include "schedule.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return VDN_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned(const void* ptr, uintptr_t n) { return (reinterpret_cast<uintptr_t>(ptr) % n) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vdn_last_error(void) { return g_last_error.c_str(); }
+
+int vdn_local_attn_num_query_blocks(int F, int tokens_per_frame, int n_text, int block_frames) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  ok();
+  return int(g.nb + (g.N > 0 ? 1 : 0));
+}
+
+int vdn_local_attn_key_intervals(int F, int tokens_per_frame, int n_text, int block_frames,
+                                 int64_t* query_rows, int64_t* key_intervals, int capacity,
+                                 int* n_qblocks) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  if (n_qblocks == nullptr) return fail(VDN_ERR_INVALID_ARG, "n_qblocks is NULL");
+  const auto blocks = vdn::build_query_blocks(g);
+  *n_qblocks = int(blocks.size());
+  if (capacity < int(blocks.size()))
+    return fail(VDN_ERR_CAPACITY, "capacity " + std::to_string(capacity) + " < " +
+                                      std::to_string(blocks.size()) + " query blocks");
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    if (query_rows != nullptr) {
+      query_rows[2 * i] = blocks[i].row_lo;
+      query_rows[2 * i + 1] = blocks[i].row_hi;
+    }
+    if (key_intervals != nullptr) {
+      int64_t* dst = key_intervals + i * VDN_MAX_KEY_INTERVALS * 2;
+      for (int j = 0; j < VDN_MAX_KEY_INTERVALS; ++j) {
+        const bool used = j < blocks[i].n_iv;
+        dst[2 * j] = used ? blocks[i].iv[j].lo : -1;
+        dst[2 * j + 1] = used ? blocks[i].iv[j].hi : -1;
+      }
+    }
+  }
+  return ok();
+}
+
+int vdn_local_attn_count_pairs(int F, int tokens_per_frame, int n_text, int block_frames,
+                               int64_t* allowed, int64_t* anchor_added) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  if (allowed == nullptr || anchor_added == nullptr)
+    return fail(VDN_ERR_INVALID_ARG, "allowed / anchor_added is NULL");
+  vdn::count_pairs(g, allowed, anchor_added);
+  return ok();
+}
+
+int vdn_local_attn_tile_schedule(int F, int tokens_per_frame, int n_text, int block_frames,
+                                 int tile_m, int32_t* out, int capacity, int* n_entries) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  if (tile_m <= 0) return fail(VDN_ERR_INVALID_ARG, "tile_m must be >= 1");
+  if (n_entries == nullptr) return fail(VDN_ERR_INVALID_ARG, "n_entries is NULL");
+  if (g.S > INT32_MAX) return fail(VDN_ERR_OVERFLOW, "S does not fit int32");
+  const auto tiles = vdn::tile_schedule(vdn::build_query_blocks(g), tile_m);
+  *n_entries = int(tiles.size());
+  if (capacity < int(tiles.size()))
+    return fail(VDN_ERR_CAPACITY, "capacity " + std::to_string(capacity) + " < " +
+                                      std::to_string(tiles.size()) + " tiles");
+  if (out == nullptr && !tiles.empty()) return fail(VDN_ERR_INVALID_ARG, "out is NULL");
+  for (size_t i = 0; i < tiles.size(); ++i) {
+    out[4 * i] = tiles[i].qblock;
+    out[4 * i + 1] = tiles[i].row0;
+    out[4 * i + 2] = tiles[i].rows;
+    out[4 * i + 3] = tiles[i].keys;
+  }
+  return ok();
+}
+
+int vdn_local_attn_kernel_tile_m(int head_dim, int dtype) {
+  if (head_dim != 64 && head_dim != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (dtype != VDN_BF16 && dtype != VDN_FP8_E4M3) return fail(VDN_ERR_UNSUPPORTED, "unknown dtype");
+  ok();
+  return vdn::kernel_tile_m(head_dim, dtype);
+}
+
+int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float* gate, void* out,
+                       int F, int tokens_per_frame, int n_text, int block_frames, int heads,
+                       int head_dim, int dtype, int batch, const float* qkv_scales,
+                       float softmax_scale, float* lse, void* hip_stream) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  if (heads <= 0 || batch <= 0)
+    return fail(VDN_ERR_INVALID_ARG, "heads and batch must be >= 1");
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(VDN_ERR_INVALID_ARG, "q, k, v and out must be non-NULL");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got " + std::to_string(head_dim) + ")");
+  if (dtype != VDN_BF16 && dtype != VDN_FP8_E4M3)
+    return fail(VDN_ERR_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
+  if (dtype == VDN_FP8_E4M3 && qkv_scales == nullptr)
+    return fail(VDN_ERR_UNSUPPORTED, "fp8 inputs need qkv_scales");
+  if (dtype == VDN_BF16 && qkv_scales != nullptr)
+    return fail(VDN_ERR_INVALID_ARG, "qkv_scales must be NULL for bf16 inputs");
+  if (!std::isfinite(softmax_scale))
+    return fail(VDN_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(VDN_ERR_ALIGNMENT, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(gate, 4) || !aligned(lse, 4) || !aligned(qkv_scales, 4))
+    return fail(VDN_ERR_ALIGNMENT, "gate, lse and qkv_scales must be 4-byte aligned");
+  // Index types: token indices and per-sample offsets in int32 inside the
+  // kernel's loops, element offsets in int64.
+  if (g.S > INT32_MAX / 2)
+    return fail(VDN_ERR_OVERFLOW, "sequence length " + std::to_string(g.S) + " too large");
+  const int64_t elems = int64_t(batch) * g.S * int64_t(heads) * int64_t(head_dim);
+  if (elems / batch / heads / head_dim != g.S || elems > (int64_t(1) << 46))
+    return fail(VDN_ERR_OVERFLOW, "tensor element count overflows");
+  if (int64_t(batch) * heads > INT32_MAX / 4096)
+    return fail(VDN_ERR_OVERFLOW, "batch * heads too large");
+
+  const size_t in_bytes = size_t(elems) * (dtype == VDN_BF16 ? 2u : 1u);
+  const size_t out_bytes = size_t(elems) * 2u;
+  const size_t gate_bytes = gate ? size_t(batch) * size_t(g.S) * size_t(heads) * 4u : 0u;
+  const size_t lse_bytes = lse ? size_t(batch) * size_t(heads) * size_t(g.S) * 4u : 0u;
+  const size_t sc_bytes = qkv_scales ? size_t(3) * size_t(heads) * 4u : 0u;
+  const void* ins[] = {q, k, v, gate, qkv_scales};
+  const size_t in_sz[] = {in_bytes, in_bytes, in_bytes, gate_bytes, sc_bytes};
+  for (int i = 0; i < 5; ++i) {
+    if (overlaps(out, out_bytes, ins[i], in_sz[i]))
+      return fail(VDN_ERR_INVALID_ARG, "out overlaps an input");
+    if (overlaps(lse, lse_bytes, ins[i], in_sz[i]))
+      return fail(VDN_ERR_INVALID_ARG, "lse overlaps an input");
+  }
+  if (overlaps(out, out_bytes, lse, lse_bytes)) return fail(VDN_ERR_INVALID_ARG, "out overlaps lse");
+
+  const auto blocks = vdn::build_query_blocks(g);
+  if (int(blocks.size()) > vdn::kMaxQueryBlocks)
+    return fail(VDN_ERR_UNSUPPORTED, std::to_string(blocks.size()) + " query blocks exceed the limit of " +
+                                         std::to_string(vdn::kMaxQueryBlocks));
+
+  const int tile_m = vdn::kernel_tile_m(head_dim, dtype);
+  vdn::FwdParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.gate = gate;
+  p.lse = lse;
+  p.scales = qkv_scales;
+  p.B = batch;
+  p.S = int32_t(g.S);
+  p.H = heads;
+  const float sm = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(head_dim)));
+  p.score_scale_log2 = float(double(sm) * 1.4426950408889634);
+  int prefix = 0;
+  int n = 0;
+  for (int bi : vdn::cost_order(blocks)) {
+    const vdn::QueryBlock& qb = blocks[size_t(bi)];
+    vdn::QBlockDesc& d = p.blk[n++];
+    d.row_lo = int32_t(qb.row_lo);
+    d.rows = int32_t(qb.row_hi - qb.row_lo);
+    d.n_keys = int32_t(qb.n_keys);
+    d.tile_prefix = prefix;
+    d.n_iv = qb.n_iv;
+    int64_t start = 0;
+    for (int i = 0; i < qb.n_iv; ++i) {
+      d.iv_start[i] = int32_t(start);
+      d.iv_delta[i] = int32_t(qb.iv[i].lo - start);
+      start += qb.iv[i].hi - qb.iv[i].lo;
+    }
+    prefix += (d.rows + tile_m - 1) / tile_m;
+  }
+  p.n_qblocks = n;
+  p.tiles_per_bh = prefix;
+  p.total_tiles = prefix * batch * heads;
+  p.per_xcd = (p.total_tiles + 7) / 8;
+
+  const int rc = vdn::launch_fwd(p, head_dim, dtype, hip_stream);
+  if (rc != 0)
+    return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+/*
+ * vdn_local_attn.h -- C ABI of the MI355X (gfx950) local-window attention
+ * forward pass: the local Softmax branch of VDN-H3 hybrid video attention.
+ *
+ * The operation (openi.cn "VDN-MiniMax-H3", section "technical principles:
+ * local exact, remote compressed"; nav.superapi.store "VDN-MiniMax-H3 -
+ * OpenVDN's Open-Source Video Generation Acceleration Solution", section
+ * "Technical Principles", items "Local Softmax Branch", "Text Dual-Branch
+ * Injection" and "Gated Fusion Mechanism"):
+ *
+ *   The sequence holds F latent frames of T tokens each (frame-major), then
+ *   N text tokens: S = F*T + N.  Frames are grouped into blocks of
+ *   `block_frames` consecutive frames starting at frame 0 (the last block may
+ *   be short).  A video query of block b attends, with exact softmax, to
+ *     - every token of blocks b-1, b, b+1 (clipped to the video),
+ *     - every token of frames 0 and F-1 (boundary anchors, visible to all),
+ *     - every text token.
+ *   A text query attends to all S tokens.  With s = scale * q.k, the output is
+ *   o_i = sum_j softmax_j(s_ij) v_j over the query's key set, optionally
+ *   multiplied by sigmoid(gate[b, i, h]).  block_frames >= F gives plain full
+ *   attention (the dense baseline).
+ *
+ * Conventions shared by every entry point:
+ *   - Return value: VDN_OK (0) or a negative vdn_status_t.  On error a message
+ *     is available from vdn_last_error() on the calling thread.  No C++
+ *     exception crosses this boundary.
+ *   - Sizes are plain ints; token offsets in outputs are int64.
+ *   - Host-only functions never touch the GPU and may be called without one.
+ */
+#ifndef VDN_LOCAL_ATTN_H
+#define VDN_LOCAL_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Canonical key lists never need more than 3 intervals ([0,T), the block
+ * window, and [(F-1)T, S)); output arrays reserve this many slots. */
+#define VDN_MAX_KEY_INTERVALS 4
+/* Largest number of query blocks (frame blocks + 1 text block) the forward
+ * kernel accepts: F <= 63 * block_frames. */
+#define VDN_MAX_QUERY_BLOCKS 64
+
+typedef enum {
+  VDN_BF16 = 0,      /* bfloat16 q/k/v                                          */
+  VDN_FP8_E4M3 = 1   /* OCP float8 e4m3fn q/k/v with per-head fp32 scales       */
+} vdn_dtype_t;
+
+typedef enum {
+  VDN_OK = 0,
+  VDN_ERR_INVALID_ARG = -1, /* non-positive size, negative n_text, NULL pointer,
+                               or output aliasing an input                      */
+  VDN_ERR_UNSUPPORTED = -2, /* head_dim not in {64,128}, unknown dtype, fp8
+                               without scales, too many query blocks            */
+  VDN_ERR_ALIGNMENT = -3,   /* q/k/v/out not 16-byte aligned, gate/lse/scales
+                               not 4-byte aligned                               */
+  VDN_ERR_OVERFLOW = -4,    /* S or a tensor's element count does not fit the
+                               kernel's index types                             */
+  VDN_ERR_HIP = -5,         /* a HIP runtime call failed (message has details) */
+  VDN_ERR_CAPACITY = -6     /* a host output array is too small                 */
+} vdn_status_t;
+
+/*
+ * Forward pass, asynchronous on `hip_stream`.
+ *
+ *   q, k, v   device, [batch, S, heads, head_dim] contiguous, dtype `dtype`
+ *             (S = F*tokens_per_frame + n_text; video tokens frame-major,
+ *             then text tokens).
+ *   gate      device, [batch, S, heads] fp32 logits, or NULL for no gate.
+ *             The output row is multiplied by 1/(1+exp(-gate)).
+ *   out       device, [batch, S, heads, head_dim] bfloat16, written in full.
+ *   F, tokens_per_frame, n_text, block_frames
+ *             frames (>=1), tokens per frame (>=1), text tokens (>=0),
+ *             frames per block (>=1; >= F selects full attention).
+ *   heads, head_dim, dtype
+ *             heads (>=1); head_dim 64 or 128; VDN_BF16 or VDN_FP8_E4M3.
+ *   batch     samples (>=1).
+ *   qkv_scales device fp32 [3][heads] (q, k, v scale of each head) for fp8:
+ *             the real value of a code c of head h is c * scale[h].
+ *             Must be NULL for bf16.
+ *   softmax_scale  score scale; <= 0 selects 1/sqrt(head_dim).
+ *   lse       device fp32 [batch, heads, S] or NULL: natural-log
+ *             log-sum-exp of the scaled scores over each query's key set.
+ *   hip_stream a hipStream_t, or NULL for the default stream.
+ *
+ * Ownership: every buffer belongs to the caller and must stay alive until the
+ * work on `hip_stream` completes.  The call allocates no device memory and
+ * does not synchronise.  `out` and `lse` must not overlap q, k, v, gate or
+ * each other.  Arguments are validated before any HIP call; a launch failure
+ * returns VDN_ERR_HIP.
+ */
+int vdn_local_attn_fwd(const void* q, const void* k, const void* v,
+                       const float* gate, void* out,
+                       int F, int tokens_per_frame, int n_text, int block_frames,
+                       int heads, int head_dim, int dtype,
+                       int batch, const float* qkv_scales, float softmax_scale,
+                       float* lse, void* hip_stream);
+
+/*
+ * Host only.  Number of query blocks for a geometry: ceil(F/block_frames)
+ * frame blocks, plus one text block when n_text > 0.  Returns the count
+ * (>= 1) or a negative vdn_status_t.
+ */
+int vdn_local_attn_num_query_blocks(int F, int tokens_per_frame, int n_text,
+                                    int block_frames);
+
+/*
+ * Host only.  The canonical key structure of every query block, in the
+ * kernel's block order (frame blocks by index, then text):
+ *   query_rows    [capacity][2] int64: half-open query token range of each
+ *                 block (may be NULL);
+ *   key_intervals [capacity][VDN_MAX_KEY_INTERVALS][2] int64: sorted,
+ *                 disjoint, non-touching half-open key token intervals; unused
+ *                 slots are -1 (may be NULL).
+ *   *n_qblocks    receives the number of blocks written.
+ * Returns VDN_ERR_CAPACITY (and sets *n_qblocks) if capacity is too small.
+ */
+int vdn_local_attn_key_intervals(int F, int tokens_per_frame, int n_text,
+                                 int block_frames, int64_t* query_rows,
+                                 int64_t* key_intervals, int capacity,
+                                 int* n_qblocks);
+
+/*
+ * Host only.  Closed-form counts per (sample, head): *allowed = number of
+ * (query, key) pairs attended; *anchor_added = video pairs present only
+ * because the key frame is an anchor (frame 0 or F-1) outside the window.
+ */
+int vdn_local_attn_count_pairs(int F, int tokens_per_frame, int n_text,
+                               int block_frames, int64_t* allowed,
+                               int64_t* anchor_added);
+
+/*
+ * Host only.  The per-(sample, head) query-tile work list in launch order
+ * (longest key list first; ties by block index, then row): entries
+ * [capacity][4] int32 = {query block, first row, rows, keys}, tiles of
+ * `tile_m` rows that never straddle a block boundary.  *n_entries receives
+ * the count; VDN_ERR_CAPACITY if capacity is too small.
+ */
+int vdn_local_attn_tile_schedule(int F, int tokens_per_frame, int n_text,
+                                 int block_frames, int tile_m, int32_t* out,
+                                 int capacity, int* n_entries);
+
+/* Query rows per tile used by the forward kernel for a head_dim / dtype pair
+ * (so callers can reproduce its schedule with vdn_local_attn_tile_schedule),
+ * or a negative vdn_status_t. */
+int vdn_local_attn_kernel_tile_m(int head_dim, int dtype);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next call into this library on the same thread. */
+const char* vdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDN_LOCAL_ATTN_H */

@@ -1,0 +1,92 @@
+"""Helpers shared by the GPU parity tests (no attention arithmetic here: the
+expected values come from the oracle)."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from block_sparse_attention_31_amd import binding as B
+from block_sparse_attention_31_amd import synth
+
+BF16_MAX_ABS = 2e-2
+FP8_MAX_ABS = 6e-2
+BF16_REL_L2 = 1e-2
+
+
+def gpu_available() -> bool:
+    return torch.cuda.is_available()
+
+
+def oracle_inputs(inp: dict):
+    """fp64 numpy copies of exactly what the GPU receives."""
+    if inp["scales"] is None:
+        q, k, v = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v"))
+    else:
+        s = inp["scales"].numpy()
+        q, k, v = (oracle.dequantize_fp8(inp[n].to(torch.float64).numpy(), s[i])
+                   for i, n in enumerate(("q", "k", "v")))
+    g = None if inp["gate"] is None else inp["gate"].to(torch.float64).numpy()
+    return q, k, v, g
+
+
+def subset_heads(inp: dict, heads):
+    """The inputs restricted to some heads (the oracle then sees H' heads)."""
+    idx = torch.tensor(list(heads))
+    out = {n: inp[n].index_select(2, idx).contiguous() for n in ("q", "k", "v")}
+    out["gate"] = None if inp["gate"] is None else inp["gate"].index_select(2, idx).contiguous()
+    out["scales"] = None if inp["scales"] is None else inp["scales"].index_select(1, idx).contiguous()
+    return out
+
+
+def run_gpu(inp: dict, w: synth.Workload, block_frames: int | None = None, lse: bool = True,
+            stream=None):
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    gate = None if inp["gate"] is None else inp["gate"].to(dev)
+    sc = None if inp["scales"] is None else inp["scales"].to(dev)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    ls = torch.full((w.B, w.H, w.S), float("nan"), dtype=torch.float32, device=dev) if lse else None
+    B.vdn_local_attn_fwd(q, k, v, gate, out, w.F, w.T, w.N,
+                         w.Bf if block_frames is None else block_frames,
+                         qkv_scales=sc, lse=ls, stream=stream)
+    torch.cuda.synchronize()
+    return out.cpu().to(torch.float64).numpy(), (ls.cpu().to(torch.float64).numpy() if lse else None)
+
+
+def sample_rows(w: synth.Workload, tile_m: int, n_random: int, seed: int, block_frames=None):
+    """Rows that cover every query block: its first and last rows, rows on
+    both sides of each tile boundary, and random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for lo, hi in oracle.query_blocks(w.F, w.T, w.N, w.Bf if block_frames is None else block_frames):
+        rows.update({lo, lo + 1, hi - 2, hi - 1})
+        for r in range(lo + tile_m, hi, tile_m):
+            rows.update({r - 1, r})
+        rows.update(int(x) for x in rng.integers(lo, hi, size=n_random))
+    return np.array(sorted(r for r in rows if 0 <= r < w.S))
+
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, rows=None, heads=None, max_abs=BF16_MAX_ABS,
+            rel_l2=BF16_REL_L2):
+    """Element-wise comparison on the requested rows/heads; returns stats."""
+    if rows is None:
+        rows = np.arange(out_ref.shape[1])
+    if heads is None:
+        heads = np.arange(out_ref.shape[2])
+    og = out_gpu[:, rows][:, :, heads]
+    orf = out_ref[:, rows][:, :, heads]
+    assert np.isfinite(og).all(), "non-finite GPU output"
+    err = np.abs(og - orf)
+    stats = {"max_abs": float(err.max()),
+             "rel_l2": float(np.linalg.norm(og - orf) / max(np.linalg.norm(orf), 1e-300))}
+    if lse_gpu is not None:
+        lg = lse_gpu[:, heads][:, :, rows]
+        lr = lse_ref[:, heads][:, :, rows]
+        stats["lse_max_abs"] = float(np.abs(lg - lr).max())
+    assert stats["max_abs"] <= max_abs, stats
+    assert stats["rel_l2"] <= rel_l2, stats
+    if lse_gpu is not None:
+        assert stats["lse_max_abs"] <= 1e-3, stats
+    return stats

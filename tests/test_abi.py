@@ -1,0 +1,173 @@
+"""CPU tests of the C ABI: the library loads and exports every declared
+symbol, the host scheduler matches the oracle bit for bit, and every invalid
+argument of the forward call returns its status code before any HIP call
+(no GPU is touched: valid launches are never attempted here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+from block_sparse_attention_31_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vdn_local_attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("library not built")
+    return B.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vdn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_api():
+    assert declared_functions() == sorted(B.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(L):
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (vdn_\w+)", nm.stdout))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(L, name) is not None
+
+
+# ---------------------------------------------------------------- scheduler
+
+SWEEP = [(F, T, N, Bf)
+         for F in (1, 2, 4, 5, 6, 10, 11, 12, 16, 20, 21, 42)
+         for T in (1, 3, 64, 1008)
+         for N in (0, 1, 16, 512)
+         for Bf in (1, 2, 5, 7)]
+
+
+@pytest.mark.parametrize("F,T,N,Bf", SWEEP)
+def test_key_intervals_bit_exact(L, F, T, N, Bf):
+    rows, ivs = B.vdn_local_attn_key_intervals(F, T, N, Bf)
+    assert rows == oracle.query_blocks(F, T, N, Bf)
+    assert ivs == oracle.key_intervals(F, T, N, Bf)
+    assert B.vdn_local_attn_count_pairs(F, T, N, Bf) == oracle.count_pairs(F, T, N, Bf)
+
+
+def test_golden_workloads(L, golden):
+    for name, g in golden["workloads"].items():
+        rows, ivs = B.vdn_local_attn_key_intervals(g["F"], g["T"], g["N"], g["Bf"])
+        assert [list(r) for r in rows] == g["query_rows"], name
+        assert [[list(p) for p in lst] for lst in ivs] == g["key_intervals"], name
+        assert B.vdn_local_attn_count_pairs(g["F"], g["T"], g["N"], g["Bf"]) == (
+            g["allowed"], g["anchor_added"]), name
+
+
+@pytest.mark.parametrize("F,T,N,Bf,M", [(11, 64, 16, 5, 128), (20, 1008, 512, 5, 128),
+                                        (42, 1008, 512, 5, 256), (3, 7, 0, 1, 4), (20, 1008, 512, 20, 128)])
+def test_tile_schedule(L, F, T, N, Bf, M):
+    tiles = B.vdn_local_attn_tile_schedule(F, T, N, Bf, M)
+    qrows = oracle.query_blocks(F, T, N, Bf)
+    ivs = oracle.key_intervals(F, T, N, Bf)
+    keys = [sum(b - a for a, b in lst) for lst in ivs]
+    covered = {}
+    for qb, r0, rows, nk in tiles:
+        lo, hi = qrows[qb]
+        assert lo <= r0 and r0 + rows <= hi and 1 <= rows <= M
+        assert nk == keys[qb]
+        for r in range(r0, r0 + rows):
+            assert r not in covered
+            covered[r] = qb
+    assert len(covered) == F * T + N
+    ks = [t[3] for t in tiles]
+    assert ks == sorted(ks, reverse=True)  # longest key list first
+
+
+def test_tile_schedule_capacity_error(L):
+    n = ctypes.c_int(0)
+    buf = (ctypes.c_int32 * 4)()
+    rc = L.vdn_local_attn_tile_schedule(20, 1008, 512, 5, 128, buf, 1, ctypes.byref(n))
+    assert rc == -6 and n.value == 164
+    assert "capacity" in B.vdn_last_error()
+
+
+def test_kernel_tile_m(L):
+    assert B.vdn_local_attn_kernel_tile_m(128, 0) > 0
+    with pytest.raises(B.VdnError):
+        B.vdn_local_attn_kernel_tile_m(96, 0)
+
+
+# ------------------------------------------------------------- error paths
+
+A = 0x10000      # fake, aligned device addresses: validation fails before
+STEP = 1 << 32   # any use, so they are never dereferenced
+
+
+def fwd_args(**kw):
+    args = dict(q=A, k=A + STEP, v=A + 2 * STEP, gate=A + 3 * STEP, out=A + 4 * STEP,
+                F=20, T=1008, N=512, Bf=5, H=32, D=128, dtype=0, batch=1,
+                scales=None, sm=0.0, lse=None, stream=None)
+    args.update(kw)
+    return args
+
+
+def call(L, a):
+    return L.vdn_local_attn_fwd(a["q"], a["k"], a["v"], a["gate"], a["out"], a["F"], a["T"], a["N"],
+                                a["Bf"], a["H"], a["D"], a["dtype"], a["batch"], a["scales"],
+                                a["sm"], a["lse"], a["stream"])
+
+
+ERROR_CASES = [
+    ("F=0", dict(F=0), -1),
+    ("T=0", dict(T=0), -1),
+    ("Bf=0", dict(Bf=0), -1),
+    ("N<0", dict(N=-1), -1),
+    ("heads=0", dict(H=0), -1),
+    ("batch=0", dict(batch=0), -1),
+    ("q NULL", dict(q=None), -1),
+    ("k NULL", dict(k=None), -1),
+    ("v NULL", dict(v=None), -1),
+    ("out NULL", dict(out=None), -1),
+    ("head_dim 96", dict(D=96), -2),
+    ("head_dim 256", dict(D=256), -2),
+    ("dtype 7", dict(dtype=7), -2),
+    ("fp8 without scales", dict(dtype=1), -2),
+    ("bf16 with scales", dict(scales=A + 6 * STEP), -1),
+    ("scale nan", dict(sm=float("nan")), -1),
+    ("q misaligned", dict(q=A + 8), -3),
+    ("out misaligned", dict(out=A + 4 * STEP + 2), -3),
+    ("gate misaligned", dict(gate=A + 3 * STEP + 2), -3),
+    ("lse misaligned", dict(lse=A + 5 * STEP + 1), -3),
+    ("S overflow", dict(F=1 << 20, T=1 << 11), -4),
+    ("elements overflow", dict(F=1 << 10, T=1 << 14, H=1 << 20), -4),
+    ("out aliases q", dict(out=A), -1),
+    ("out inside v", dict(out=A + 2 * STEP + 4096), -1),
+    ("lse aliases gate", dict(lse=A + 3 * STEP), -1),
+    ("lse inside out", dict(lse=A + 4 * STEP + 64), -1),
+    ("too many query blocks", dict(F=400, T=4, N=0, Bf=1), -2),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", ERROR_CASES, ids=[c[0] for c in ERROR_CASES])
+def test_forward_argument_errors(L, name, kw, code):
+    rc = call(L, fwd_args(**kw))
+    assert rc == code, (name, rc, B.vdn_last_error())
+    assert B.vdn_last_error() != ""
+
+
+def test_host_function_errors(L):
+    with pytest.raises(B.VdnError) as e:
+        B.vdn_local_attn_key_intervals(0, 4, 0, 5)
+    assert e.value.status == -1
+    with pytest.raises(B.VdnError):
+        B.vdn_local_attn_count_pairs(4, 4, -2, 5)
+    with pytest.raises(B.VdnError):
+        B.vdn_local_attn_tile_schedule(4, 4, 0, 5, 0)
+    n = ctypes.c_int(0)
+    rc = L.vdn_local_attn_key_intervals(20, 10, 4, 5, None, None, 2, ctypes.byref(n))
+    assert rc == -6 and n.value == 5

@@ -1,0 +1,207 @@
+"""GPU parity of the HIP forward pass (through the C ABI) against the CPU
+oracle, on the same seeded inputs.
+
+Bars: bf16 max-abs 2e-2 and relative L2 1e-2; fp8 max-abs 6e-2 (inputs
+~N(0,1)); log-sum-exp within 1e-3; key-set structure checked exactly through
+the log-sum-exp of zero queries and through needle probes."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_31_amd import binding as B
+from block_sparse_attention_31_amd import synth
+
+from .gpu_util import (FP8_MAX_ABS, compare, gpu_available, oracle_inputs, run_gpu, sample_rows,
+                       subset_heads)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _tile_m(w):
+    return B.vdn_local_attn_kernel_tile_m(w.D, 0 if w.dtype == "bf16" else 1)
+
+
+def _log(name, stats):
+    print(f"[parity] {name}: " + ", ".join(f"{k}={v:.3g}" for k, v in stats.items()), flush=True)
+
+
+# -------------------------------------------------------- full comparisons
+
+def test_tiny_full():
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w)
+    orf, lrf = oracle.attend(*oracle_inputs(inp), w.F, w.T, w.N, w.Bf)
+    _log("tiny", compare(og, lg, orf, lrf))
+
+
+RANDOM_SHAPES = [
+    # B, H, D, F, T, N, Bf, gate
+    (1, 2, 64, 7, 48, 8, 2, True),
+    (2, 3, 128, 9, 37, 5, 2, True),      # T not a multiple of anything
+    (1, 2, 128, 1, 200, 0, 5, False),    # one frame, no text
+    (1, 1, 64, 16, 64, 0, 5, True),      # no text
+    (1, 2, 128, 12, 130, 70, 3, False),
+    (1, 1, 64, 30, 5, 3, 1, True),       # one-frame blocks, tiny frames
+    (1, 2, 128, 6, 100, 300, 5, True),   # text block larger than a tile
+    (1, 1, 128, 5, 1, 1, 5, True),       # S = 6 (single partial tile)
+    (2, 1, 64, 11, 64, 16, 11, True),    # block covers the video: dense
+]
+
+
+@pytest.mark.parametrize("Bt,H,D,F,T,N,Bf,gate", RANDOM_SHAPES)
+def test_random_shapes_full(Bt, H, D, F, T, N, Bf, gate):
+    w = synth.random_workload(seed=100 + F * 7 + T, B=Bt, H=H, D=D, F=F, T=T, N=N, Bf=Bf, gate=gate)
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w)
+    orf, lrf = oracle.attend(*oracle_inputs(inp), w.F, w.T, w.N, w.Bf)
+    _log(f"rand {Bt,H,D,F,T,N,Bf,gate}", compare(og, lg, orf, lrf))
+
+
+def test_outliers_and_scale():
+    """2% outlier channels x8 and an explicit softmax scale."""
+    w = synth.random_workload(seed=7, H=2, D=128, F=8, T=96, N=24, Bf=2, outlier_frac=0.02)
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.S), device=dev)
+    B.vdn_local_attn_fwd(q, k, v, inp["gate"].to(dev), out, w.F, w.T, w.N, w.Bf,
+                         softmax_scale=0.05, lse=lse)
+    torch.cuda.synchronize()
+    orf, lrf = oracle.attend(*oracle_inputs(inp), w.F, w.T, w.N, w.Bf, scale=0.05)
+    _log("outliers", compare(out.cpu().double().numpy(), lse.cpu().double().numpy(), orf, lrf))
+
+
+# ------------------------------------------- full-size workloads, sampled
+
+@pytest.mark.parametrize("name", ["medium", "768p", "long"])
+def test_workload_sampled(name):
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w)
+    rows = sample_rows(w, _tile_m(w), n_random=6, seed=5)
+    heads = sorted({0, w.H - 1, w.H // 2})
+    orf, lrf = oracle.attend(*oracle_inputs(subset_heads(inp, heads)), w.F, w.T, w.N, w.Bf, rows=rows)
+    _log(name, compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows))
+    # every output element is finite
+    assert np.isfinite(og).all()
+
+
+def test_768p_dense_mode_sampled():
+    """block_frames = F: the same kernel computes full attention."""
+    w = synth.WORKLOADS["768p"]
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w, block_frames=w.F)
+    rows = sample_rows(w, _tile_m(w), n_random=8, seed=6, block_frames=w.F)
+    heads = [3, 17]
+    orf, lrf = oracle.attend(*oracle_inputs(subset_heads(inp, heads)), w.F, w.T, w.N, w.F, rows=rows)
+    _log("768p dense", compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows))
+
+
+# ------------------------------------------------------ structure checks
+
+@pytest.mark.parametrize("name", ["tiny", "768p", "long"])
+def test_key_counts_exact_via_lse(name):
+    """With q = 0 every key scores 0, so lse = ln |K(i)|: the number of keys
+    each query visited, recovered exactly, equals the closed-form count."""
+    w = synth.WORKLOADS[name]
+    shape = (w.B, w.S, 2, w.D)
+    dev = torch.device("cuda:0")
+    q = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+    k = torch.randn(shape, device=dev).to(torch.bfloat16)
+    v = torch.randn(shape, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, 2, w.S), device=dev)
+    B.vdn_local_attn_fwd(q, k, v, None, out, w.F, w.T, w.N, w.Bf, lse=lse)
+    torch.cuda.synchronize()
+    counts = torch.exp(lse.double()).round().cpu().numpy()
+    expect = np.zeros(w.S)
+    for (lo, hi), ivs in zip(oracle.query_blocks(w.F, w.T, w.N, w.Bf),
+                             oracle.key_intervals(w.F, w.T, w.N, w.Bf)):
+        expect[lo:hi] = sum(b - a for a, b in ivs)
+    assert (counts == expect[None, None, :]).all()
+    # q = 0 also makes the output the plain mean of v over the key set
+    rows = sample_rows(w, _tile_m(w), n_random=2, seed=1)
+    vv = v[:, :, :, :].double().cpu().numpy()
+    for (lo, hi), ivs in zip(oracle.query_blocks(w.F, w.T, w.N, w.Bf),
+                             oracle.key_intervals(w.F, w.T, w.N, w.Bf)):
+        keys = np.concatenate([np.arange(a, b) for a, b in ivs])
+        mean = vv[:, keys].mean(axis=1)  # [B, H, D]
+        r = rows[(rows >= lo) & (rows < hi)]
+        got = out[:, r].double().cpu().numpy()
+        assert np.abs(got - mean[:, None]).max() < 4e-3
+
+
+def test_needle_probes_768p_geometry():
+    """A query equal to alpha * k_j scores key j far above every other key:
+    the output is v_j when j is visible and far from it when not.  Cases sit
+    on every interval edge of the 768p geometry (F=20, T=1008, N=512)."""
+    F, T, N, Bf, H, D = 20, 1008, 512, 5, 2, 128
+    S = F * T + N
+    tok = lambda f, j=0: f * T + j  # noqa: E731
+    V = F * T
+    cases = [
+        (tok(2), tok(9, T - 1), True), (tok(2, 1), tok(10), False),
+        (tok(2, 2), tok(19), True), (tok(2, 3), tok(18, T - 1), False),
+        (tok(7), tok(0), True), (tok(7, 1), tok(14, T - 1), True), (tok(7, 2), tok(15), False),
+        (tok(7, 3), tok(19, T - 1), True),
+        (tok(12), tok(4, T - 1), False), (tok(12, 1), tok(5), True), (tok(12, 2), tok(0, T - 1), True),
+        (tok(12, 3), tok(1), False), (tok(17), tok(9, T - 1), False), (tok(17, 1), tok(10), True),
+        (tok(19, 5), tok(5), False), (tok(19, 6), V, True), (tok(0, 9), S - 1, True),
+        (V, tok(12, 3), True), (S - 1, tok(19, T - 1), True), (V + 7, 0, True),
+        (tok(4, T - 1), tok(10), False), (tok(5), tok(14, T - 1), True),  # block edges
+    ]
+    g = torch.Generator().manual_seed(3)
+    k = torch.randn((1, S, H, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((1, S, H, D), generator=g).to(torch.bfloat16)
+    pairs = [(0, i, h, j) for (i, j, _) in cases for h in range(H)]
+    q = synth.needle_queries(k, pairs, alpha=6.0)
+    dev = torch.device("cuda:0")
+    out = torch.empty((1, S, H, D), dtype=torch.bfloat16, device=dev)
+    B.vdn_local_attn_fwd(q.to(dev), k.to(dev), v.to(dev), None, out, F, T, N, Bf)
+    torch.cuda.synchronize()
+    o = out.cpu().double()
+    for i, j, visible in cases:
+        for h in range(H):
+            err = (o[0, i, h] - v[0, j, h].double()).abs().max().item()
+            if visible:
+                assert err < 0.05, (i, j, h, err)
+            else:
+                assert err > 0.5, (i, j, h, err)
+
+
+# ------------------------------------------------------- run properties
+
+def test_deterministic_and_stream():
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(w)
+    a, la = run_gpu(inp, w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b, lb = run_gpu(inp, w, stream=s.cuda_stream)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_gate_none_vs_zero_logits():
+    w = synth.random_workload(seed=11, H=2, D=128, F=6, T=64, N=16, Bf=2)
+    inp = synth.make_inputs(w)
+    inp0 = dict(inp, gate=torch.zeros_like(inp["gate"]))
+    inpn = dict(inp, gate=None)
+    o0, _ = run_gpu(inp0, w)
+    on, _ = run_gpu(inpn, w)
+    # sigmoid(0) = 1/2 exactly; halving is exact in bf16 away from underflow
+    assert np.array_equal(o0, on * 0.5)
+
+
+def test_bad_arguments_raise_without_launch():
+    dev = torch.device("cuda:0")
+    q = torch.zeros((1, 10, 1, 96), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(B.VdnError) as e:
+        B.vdn_local_attn_fwd(q, q.clone(), q.clone(), None, torch.empty_like(q), 2, 5, 0, 5)
+    assert e.value.status == -2
