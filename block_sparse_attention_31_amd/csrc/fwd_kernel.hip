@@ -34,6 +34,7 @@ namespace vdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -55,6 +56,11 @@ __device__ __forceinline__ int vt_pos(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
+// Online-softmax reference point may lag the running maximum by up to 2^8 in
+// the base-2 domain: P then stays below 256, exact in bf16 up to rounding,
+// and the accumulator rescale is skipped unless the maximum grows by more.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, int QB>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
   constexpr int NW = 4;
@@ -69,10 +75,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
   constexpr int NDS = D / 16;     // k-steps of the QK^T MFMA
   constexpr int NDB = D / 32;     // 32-wide d blocks of the output
   constexpr int NKB = KT / 32;    // 32-key blocks per step
+  constexpr int KBUF = KT * KP;
+  constexpr int VBUF = D * VP;
   static_assert(KCH >= 1 && VITEMS <= 256, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[KT * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[D * VP];
+  // Two LDS buffers: step s computes from buffer s&1 while step s+1's tile
+  // is staged into the other one.
+  __shared__ __attribute__((aligned(16))) __bf16 Ks[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) __bf16 Vt[2 * VBUF];
 
   // ---- which tile: XCD-aware remap so that consecutive tiles of one
   // (sample, head) land on the same XCD (workgroups are dealt round-robin
@@ -98,9 +108,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
   const int hh = lane >> 5;
 
   const int64_t rs = int64_t(p.H) * D;  // token stride (elements)
-  const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q) + int64_t(b) * p.S * rs + int64_t(h) * D;
-  const __bf16* __restrict__ kg = static_cast<const __bf16*>(p.k) + int64_t(b) * p.S * rs + int64_t(h) * D;
-  const __bf16* __restrict__ vg = static_cast<const __bf16*>(p.v) + int64_t(b) * p.S * rs + int64_t(h) * D;
+  const int64_t bh_off = int64_t(b) * p.S * rs + int64_t(h) * D;
+  const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q) + bh_off;
+  const char* __restrict__ kg = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.k) + bh_off);
+  const char* __restrict__ vg = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.v) + bh_off);
 
   // ---- Q rows for this wave, kept in registers as MFMA B operands.
   bf16x8 qreg[QB][NDS];
@@ -129,67 +140,112 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
   }
 
-  // ---- global -> register staging of one K/V step
-  u32x4 kst[KCH];
-  u32x4 vst[4];
+  // ---- global -> register staging of one K/V step.  Per-thread byte
+  // offsets relative to the tile's first key are fixed; a tile that lies
+  // inside one key interval is addressed from a scalar base.
+  const int64_t rsb = rs * 2;  // token stride in bytes
+  constexpr int KROWS = 256 / DC;  // key rows covered by one K chunk pass
+  const int k_r0 = tid / DC;
+  const uint32_t k_off = uint32_t(k_r0 * rsb + (tid - k_r0 * DC) * 16);
   const int v_kq = tid % (KT / 4);
   const int v_cc = tid / (KT / 4);
-  auto load_step = [&](int step) {
+  const uint32_t v_off = uint32_t(v_kq * 4 * rsb + v_cc * 16);
+
+  u32x4 kst[KCH];
+  u32x4 vst[4];
+  int iv = 0;  // interval holding the current step's first key
+  int64_t tile_base = 0;  // byte offset of the step's first key (fast path)
+  bool fast = true;
+  // Decide how the step's 64 keys are addressed: from one scalar base when
+  // they lie inside one key interval, else key by key.
+  auto plan_step = [&](int step) {
     const int j0 = step * KT;
+    while (iv + 1 < d.n_iv && j0 >= d.iv_start[iv + 1]) ++iv;
+    const int iv_end = (iv + 1 < d.n_iv) ? d.iv_start[iv + 1] : n_keys;
+    fast = j0 + KT <= iv_end;
+    tile_base = int64_t(j0 + d.iv_delta[iv]) * rsb;
+  };
+  auto load_k = [&](int step) {
+    if (fast) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int u = c * 256 + tid;
-      const int kr = u / DC;
-      const int cc = u - kr * DC;
-      const int j = j0 + kr;
-      if (j < n_keys) {
-        kst[c] = *reinterpret_cast<const u32x4*>(kg + int64_t(vtoken(d, j)) * rs + cc * 8);
-      } else {
-        kst[c] = u32x4{0u, 0u, 0u, 0u};
+      for (int c = 0; c < KCH; ++c)
+        kst[c] = *reinterpret_cast<const u32x4*>(kg + (tile_base + c * KROWS * rsb) + k_off);
+    } else {
+      const int j0 = step * KT;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const int j = j0 + c * KROWS + k_r0;
+        if (j < n_keys) {
+          kst[c] = *reinterpret_cast<const u32x4*>(kg + int64_t(vtoken(d, j)) * rsb +
+                                                    (k_off - uint32_t(k_r0 * rsb)));
+        } else {
+          kst[c] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
-    if (tid < VITEMS) {
+  };
+  auto load_v = [&](int step) {
+    if (tid >= VITEMS) return;
+    if (fast) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vst[i] = *reinterpret_cast<const u32x4*>(vg + (tile_base + i * rsb) + v_off);
+    } else {
+      const int j0 = step * KT;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = j0 + v_kq * 4 + i;
         if (j < n_keys) {
-          vst[i] = *reinterpret_cast<const u32x4*>(vg + int64_t(vtoken(d, j)) * rs + v_cc * 8);
+          vst[i] = *reinterpret_cast<const u32x4*>(vg + int64_t(vtoken(d, j)) * rsb + v_cc * 16);
         } else {
           vst[i] = u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
   };
-  auto store_step = [&]() {
+  auto store_k = [&](int buf) {
+    __bf16* ks = Ks + buf * KBUF;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int u = c * 256 + tid;
       const int kr = u / DC;
       const int cc = u - kr * DC;
-      *reinterpret_cast<u32x4*>(&Ks[kr * KP + cc * 8]) = kst[c];
+      *reinterpret_cast<u32x4*>(&ks[kr * KP + cc * 8]) = kst[c];
     }
-    if (tid < VITEMS) {
-      // 4 keys x 8 d in registers -> 8 rows of V^T, 4 keys (8 bytes) each.
-      const int pos = vt_pos(v_kq * 4);
+  };
+  auto store_v = [&](int buf) {
+    if (tid >= VITEMS) return;
+    __bf16* vt = Vt + buf * VBUF;
+    // 4 keys x 8 d in registers -> 8 rows of V^T, 4 keys (8 bytes) each.
+    const int pos = vt_pos(v_kq * 4);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t a0 = vst[0][m], a1 = vst[1][m], a2 = vst[2][m], a3 = vst[3][m];
-        const u32x2 even = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        const u32x2 odd = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        *reinterpret_cast<u32x2*>(&Vt[(v_cc * 8 + 2 * m) * VP + pos]) = even;
-        *reinterpret_cast<u32x2*>(&Vt[(v_cc * 8 + 2 * m + 1) * VP + pos]) = odd;
-      }
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t a0 = vst[0][m], a1 = vst[1][m], a2 = vst[2][m], a3 = vst[3][m];
+      const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+      const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+      *reinterpret_cast<u32x2*>(&vt[(v_cc * 8 + 2 * m) * VP + pos]) = even;
+      *reinterpret_cast<u32x2*>(&vt[(v_cc * 8 + 2 * m + 1) * VP + pos]) = odd;
     }
   };
 
   const float c = p.score_scale_log2;
   const int nsteps = (n_keys + KT - 1) / KT;
 
-  load_step(0);
+  plan_step(0);
+  load_k(0);
+  load_v(0);
+  store_k(0);
+  store_v(0);
+  __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
-    store_step();
-    __syncthreads();
-    if (step + 1 < nsteps) load_step(step + 1);
+    const int buf = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) {
+      plan_step(step + 1);
+      load_k(step + 1);
+    }
+    const __bf16* ks = Ks + buf * KBUF;
+    const __bf16* vt = Vt + buf * VBUF;
 
     // ---- S^T = K Q^T for KT keys x QW queries
     f32x16 s[NKB][QB];
@@ -201,11 +257,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
     for (int ds = 0; ds < NDS; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + lr) * KP + ds * 16 + hh * 8]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[(kb * 32 + lr) * KP + ds * 16 + hh * 8]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ds], s[kb][qb], 0, 0, 0);
       }
+    }
+
+    // K of the next step goes to the other buffer (last read one step ago,
+    // before the barrier that ended it); then fetch V of the next step.
+    if (more) {
+      store_k(buf ^ 1);
+      load_v(step + 1);
     }
 
     // ---- mask the tail of the key list
@@ -223,19 +286,28 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
         }
     }
 
-    // ---- online softmax (base-2, scale folded into c)
+    // ---- online softmax (base-2, scale folded into c, lazy rescale)
     bf16x8 pk[QB][NKB][2];
+    const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[0][qb][0];
+      float mx = fmaxf(s[0][qb][0], s[0][qb][1]);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[qb], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][qb][r], s[kb][qb][r + 1]));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      if (__any(mx > m_run[qb] + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run[qb], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+      }
+      const float mneg = -m_run[qb];
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -243,19 +315,17 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
         for (int half = 0; half < 2; ++half) {
           bf16x8 v8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][half * 8 + e], c, -m_new));
-            lsum += pe;
-            v8[e] = static_cast<__bf16>(pe);
-          }
+          for (int e = 0; e < 8; ++e)
+            v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][half * 8 + e], c, mneg)));
           pk[qb][kb][half] = v8;
+          // the denominator sums the same rounded weights that enter P V
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 0, 1), kOnes2, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 2, 3), kOnes2, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 4, 5), kOnes2, lsum, false);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 6, 7), kOnes2, lsum, false);
         }
       }
-      l_run[qb] = l_run[qb] * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+      l_run[qb] += lsum;
     }
 
     // ---- O^T += V^T P^T
@@ -265,18 +335,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[(db * 32 + lr) * VP + kb * 32 + half * 16 + hh * 8]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(db * 32 + lr) * VP + kb * 32 + half * 16 + hh * 8]);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[qb][kb][half], acc[qb][db], 0, 0, 0);
         }
       }
     }
+    if (more) store_v(buf ^ 1);
     __syncthreads();
   }
 
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
-  __bf16* og = static_cast<__bf16*>(p.out) + int64_t(b) * p.S * rs + int64_t(h) * D;
+  __bf16* og = static_cast<__bf16*>(p.out) + bh_off;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int lrow = wave * QW + qb * 32 + lr;
