@@ -61,16 +61,18 @@ __device__ __forceinline__ int vt_pos(int r) {
 // and the accumulator rescale is skipped unless the maximum grows by more.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int QB>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
-  constexpr int NW = 4;
+template <int D, int QB, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p) {
   constexpr int QW = 32 * QB;     // query rows per wave
   constexpr int M = NW * QW;      // query rows per workgroup
   constexpr int KT = 64;          // keys per step
   constexpr int KP = D + 8;       // K tile row pitch (bf16), 16-byte pad
   constexpr int VP = KT + 8;      // V^T tile row pitch (bf16), 16-byte pad
   constexpr int DC = D / 8;       // 16-byte chunks per row
-  constexpr int KCH = KT * DC / 256;          // K chunks per thread
+  // Staging: threads [K0, K0 + 256) load K, threads [0, 256) load V (with 8
+  // waves the two halves of the workgroup split the work).
+  constexpr int K0 = NW > 4 ? 256 : 0;
+  constexpr int KCH = KT * DC / 256;          // K chunks per K thread
   constexpr int VITEMS = (KT / 4) * DC;       // (4 keys x 8 d) V items
   constexpr int NDS = D / 16;     // k-steps of the QK^T MFMA
   constexpr int NDB = D / 32;     // 32-wide d blocks of the output
@@ -145,31 +147,36 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
   // inside one key interval is addressed from a scalar base.
   const int64_t rsb = rs * 2;  // token stride in bytes
   constexpr int KROWS = 256 / DC;  // key rows covered by one K chunk pass
-  const int k_r0 = tid / DC;
-  const uint32_t k_off = uint32_t(k_r0 * rsb + (tid - k_r0 * DC) * 16);
+  const int ktid = tid - K0;
+  const bool k_loader = ktid >= 0 && ktid < 256;
+  const int k_r0 = ktid / DC;
+  const uint32_t k_off = uint32_t(k_r0 * rsb + (ktid - k_r0 * DC) * 16);
   const int v_kq = tid % (KT / 4);
   const int v_cc = tid / (KT / 4);
   const uint32_t v_off = uint32_t(v_kq * 4 * rsb + v_cc * 16);
 
   u32x4 kst[KCH];
   u32x4 vst[4];
-  int iv = 0;  // interval holding the current step's first key
-  int64_t tile_base = 0;  // byte offset of the step's first key (fast path)
-  bool fast = true;
-  // Decide how the step's 64 keys are addressed: from one scalar base when
-  // they lie inside one key interval, else key by key.
-  auto plan_step = [&](int step) {
+  // How a step's KT keys are addressed: from one scalar base when they lie
+  // inside one key interval (the common case), else key by key.  K runs two
+  // steps ahead of the softmax and V one step ahead, so each keeps its own
+  // interval cursor.
+  struct Plan {
+    bool fast;
+    int64_t base;  // byte offset of the step's first key (fast path)
+  };
+  auto plan = [&](int step, int& iv) -> Plan {
     const int j0 = step * KT;
     while (iv + 1 < d.n_iv && j0 >= d.iv_start[iv + 1]) ++iv;
     const int iv_end = (iv + 1 < d.n_iv) ? d.iv_start[iv + 1] : n_keys;
-    fast = j0 + KT <= iv_end;
-    tile_base = int64_t(j0 + d.iv_delta[iv]) * rsb;
+    return Plan{j0 + KT <= iv_end, int64_t(j0 + d.iv_delta[iv]) * rsb};
   };
-  auto load_k = [&](int step) {
-    if (fast) {
+  auto load_k = [&](int step, const Plan& pl) {
+    if (!k_loader) return;
+    if (pl.fast) {
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
-        kst[c] = *reinterpret_cast<const u32x4*>(kg + (tile_base + c * KROWS * rsb) + k_off);
+        kst[c] = *reinterpret_cast<const u32x4*>(kg + (pl.base + c * KROWS * rsb) + k_off);
     } else {
       const int j0 = step * KT;
 #pragma unroll
@@ -184,12 +191,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
       }
     }
   };
-  auto load_v = [&](int step) {
+  auto load_v = [&](int step, const Plan& pl) {
     if (tid >= VITEMS) return;
-    if (fast) {
+    if (pl.fast) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        vst[i] = *reinterpret_cast<const u32x4*>(vg + (tile_base + i * rsb) + v_off);
+        vst[i] = *reinterpret_cast<const u32x4*>(vg + (pl.base + i * rsb) + v_off);
     } else {
       const int j0 = step * KT;
 #pragma unroll
@@ -204,10 +211,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
     }
   };
   auto store_k = [&](int buf) {
+    if (!k_loader) return;
     __bf16* ks = Ks + buf * KBUF;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-      const int u = c * 256 + tid;
+      const int u = c * 256 + ktid;
       const int kr = u / DC;
       const int cc = u - kr * DC;
       *reinterpret_cast<u32x4*>(&ks[kr * KP + cc * 8]) = kst[c];
@@ -230,25 +238,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
 
   const float c = p.score_scale_log2;
   const int nsteps = (n_keys + KT - 1) / KT;
+  const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  plan_step(0);
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      plan_step(step + 1);
-      load_k(step + 1);
-    }
+  // S^T = K Q^T for the KT keys in K buffer `buf`.
+  auto qk = [&](int buf, f32x16 (&s)[NKB][QB]) {
     const __bf16* ks = Ks + buf * KBUF;
-    const __bf16* vt = Vt + buf * VBUF;
-
-    // ---- S^T = K Q^T for KT keys x QW queries
-    f32x16 s[NKB][QB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -263,15 +257,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ds], s[kb][qb], 0, 0, 0);
       }
     }
+  };
 
-    // K of the next step goes to the other buffer (last read one step ago,
-    // before the barrier that ended it); then fetch V of the next step.
-    if (more) {
-      store_k(buf ^ 1);
-      load_v(step + 1);
-    }
+  // One step of the software pipeline: softmax of step `step` (scores in
+  // s_cur) and P V with V buffer step&1, while the MFMA units compute the
+  // scores of step+1 into s_next from K buffer (step+1)&1.  On the last step
+  // that product reads a stale buffer and is discarded.
+  int ivk = 0, ivv = 0;
+  auto body = [&](int step, f32x16 (&s_cur)[NKB][QB], f32x16 (&s_next)[NKB][QB]) {
+    const int buf = step & 1;
+    const bool has1 = step + 1 < nsteps;
+    const bool has2 = step + 2 < nsteps;
+    if (has2) load_k(step + 2, plan(step + 2, ivk));
+    if (has1) load_v(step + 1, plan(step + 1, ivv));
 
-    // ---- mask the tail of the key list
+    // mask the tail of the key list
     const int j0 = step * KT;
     if (j0 + KT > n_keys) {
 #pragma unroll
@@ -281,21 +281,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
           const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
           if (j >= n_keys) {
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb][r] = -__builtin_inff();
+            for (int qb = 0; qb < QB; ++qb) s_cur[kb][qb][r] = -__builtin_inff();
           }
         }
     }
-
-    // ---- online softmax (base-2, scale folded into c, lazy rescale)
-    bf16x8 pk[QB][NKB][2];
-    const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    // running maximum; rescale only when it grew by more than the slack
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(s[0][qb][0], s[0][qb][1]);
+      float mx = fmaxf(s_cur[0][qb][0], s_cur[0][qb][1]);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][qb][r], s[kb][qb][r + 1]));
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2)
+          mx = fmaxf(mx, fmaxf(s_cur[kb][qb][r], s_cur[kb][qb][r + 1]));
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
       if (__any(mx > m_run[qb] + kRescaleSlack)) {
         const float m_new = fmaxf(m_run[qb], mx);
@@ -307,6 +305,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
       }
+    }
+
+    // scores of the next step (independent of the softmax below)
+    qk(buf ^ 1, s_next);
+
+    // P = exp2(S c - m), packed to bf16; row sums over the rounded weights
+    bf16x8 pk[QB][NKB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       const float mneg = -m_run[qb];
       float lsum = 0.f;
 #pragma unroll
@@ -316,9 +323,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
           bf16x8 v8;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][half * 8 + e], c, mneg)));
+            v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][qb][half * 8 + e], c, mneg)));
           pk[qb][kb][half] = v8;
-          // the denominator sums the same rounded weights that enter P V
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 0, 1), kOnes2, lsum, false);
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 2, 3), kOnes2, lsum, false);
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 4, 5), kOnes2, lsum, false);
@@ -328,7 +334,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
       l_run[qb] += lsum;
     }
 
-    // ---- O^T += V^T P^T
+    // O^T += V^T P^T
+    const __bf16* vt = Vt + buf * VBUF;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -342,8 +349,31 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
         }
       }
     }
-    if (more) store_v(buf ^ 1);
+
+    // K of step+2 replaces K of step (read one step ago, before the last
+    // barrier); V of step+1 replaces V of step-1.
+    if (has2) store_k(buf);
+    if (has1) store_v(buf ^ 1);
     __syncthreads();
+  };
+
+  // prologue: K of steps 0 and 1, V of step 0, scores of step 0
+  load_k(0, plan(0, ivk));
+  load_v(0, plan(0, ivv));
+  store_k(0);
+  store_v(0);
+  if (nsteps > 1) {
+    load_k(1, plan(1, ivk));
+    store_k(1);
+  }
+  __syncthreads();
+  f32x16 sA[NKB][QB], sB[NKB][QB];
+  qk(0, sA);
+  for (int step = 0;;) {
+    body(step, sA, sB);
+    if (++step >= nsteps) break;
+    body(step, sB, sA);
+    if (++step >= nsteps) break;
   }
 
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
@@ -377,21 +407,24 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const FwdParams p) {
   }
 }
 
+// Waves per workgroup of the bf16 kernel: each wave owns 32 query rows.
+constexpr int kWaves = 8;
+
 int kernel_tile_m(int head_dim, int dtype) {
   (void)head_dim;
   (void)dtype;
-  return 128;
+  return 32 * kWaves;
 }
 
 int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
   const dim3 grid(unsigned(p.per_xcd) * 8u);
-  const dim3 block(256);
+  const dim3 block(64 * kWaves);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype != 0) return int(hipErrorInvalidValue);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 1>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, 1, kWaves>), grid, block, 0, st, p);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, 1>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, 1, kWaves>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
