@@ -30,6 +30,8 @@
 
 #include "fwd_params.hpp"
 
+#include <type_traits>
+
 namespace vdn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -49,42 +51,56 @@ __device__ __forceinline__ int vtoken(const QBlockDesc& d, int j) {
   return t;
 }
 
-// Position of key r (0..KT-1) inside the transposed V tile: bits 2 and 3
-// swapped, so that within each group of 16 keys the two half-waves' key sets
-// {0-3, 8-11} and {4-7, 12-15} become contiguous runs of 8.
-__device__ __forceinline__ int vt_pos(int r) {
-  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
-
 // Online-softmax reference point may lag the running maximum by up to 2^8 in
 // the base-2 domain: P then stays below 256, exact in bf16 up to rounding,
 // and the accumulator rescale is skipped unless the maximum grows by more.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int QB, int NW>
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+
+#define VDN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// K and V stream through a ring of NS LDS stages filled by
+// global_load_lds_dwordx4 (16 bytes per lane, written to LDS at lane*16 of a
+// wave-uniform base), NS-1 steps ahead of use; no register staging.  Rows are
+// stored unpadded, 16-byte chunks XOR-swizzled so that fragment reads hit
+// distinct banks:
+//   K: chunk c of key row r is stored at chunk c ^ (r % (D/8)) -- the 32 rows
+//      of a QK^T A-operand read are spread over all chunks;
+//   V: chunk c of key row r is stored at chunk c ^ 2(r % 4) -- the four rows of
+//      a ds_read_b64_tr_b16 land on different 32-byte bank groups.
+// V^T fragments come from two ds_read_b64_tr_b16 per MFMA: in each group of
+// 16 lanes, lane i receives element (i % 4) of the 8-byte blocks addressed by
+// lanes 4e + i/4 (e = 0..3), so if those lanes point at keys k+e, columns
+// d0 + 4(i/4).., lane i holds V[k..k+3][d0 + i]: the MFMA A-operand layout.
+template <int D, int NW, int NS>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p) {
-  constexpr int QW = 32 * QB;     // query rows per wave
-  constexpr int M = NW * QW;      // query rows per workgroup
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int KT = 64;          // keys per step
-  constexpr int KP = D + 8;       // K tile row pitch (bf16), 16-byte pad
-  constexpr int VP = KT + 8;      // V^T tile row pitch (bf16), 16-byte pad
-  constexpr int DC = D / 8;       // 16-byte chunks per row
-  // Staging: threads [K0, K0 + 256) load K, threads [0, 256) load V (with 8
-  // waves the two halves of the workgroup split the work).
-  constexpr int K0 = NW > 4 ? 256 : 0;
-  constexpr int KCH = KT * DC / 256;          // K chunks per K thread
-  constexpr int VITEMS = (KT / 4) * DC;       // (4 keys x 8 d) V items
+  constexpr int QW = 32;          // query rows per wave
+  constexpr int M = NW * QW;      // query rows per workgroup
+  constexpr int RB = 2 * D;       // bytes per key row
+  constexpr int CH = D / 8;       // 16-byte chunks per row
+  constexpr int TILE = KT * RB;   // bytes per K (or V) stage
+  constexpr int NI = TILE / 1024 / NW;  // DMA instructions per wave per tensor per step
+  constexpr int RPI = 1024 / RB;  // key rows per DMA instruction
   constexpr int NDS = D / 16;     // k-steps of the QK^T MFMA
   constexpr int NDB = D / 32;     // 32-wide d blocks of the output
   constexpr int NKB = KT / 32;    // 32-key blocks per step
-  constexpr int KBUF = KT * KP;
-  constexpr int VBUF = D * VP;
-  static_assert(KCH >= 1 && VITEMS <= 256, "tile shape");
+  static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
+  static_assert(NS == 4, "the main loop is unrolled for a 4-stage ring");
 
-  // Two LDS buffers: step s computes from buffer s&1 while step s+1's tile
-  // is staged into the other one.
-  __shared__ __attribute__((aligned(16))) __bf16 Ks[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) __bf16 Vt[2 * VBUF];
+  __shared__ __attribute__((aligned(1024))) char Ks[NS * TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs[NS * TILE];
 
   // ---- which tile: XCD-aware remap so that consecutive tiles of one
   // (sample, head) land on the same XCD (workgroups are dealt round-robin
@@ -110,166 +126,136 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   const int hh = lane >> 5;
 
   const int64_t rs = int64_t(p.H) * D;  // token stride (elements)
+  const int64_t rsb = rs * 2;           // token stride (bytes)
   const int64_t bh_off = int64_t(b) * p.S * rs + int64_t(h) * D;
   const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q) + bh_off;
   const char* __restrict__ kg = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.k) + bh_off);
   const char* __restrict__ vg = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.v) + bh_off);
 
   // ---- Q rows for this wave, kept in registers as MFMA B operands.
-  bf16x8 qreg[QB][NDS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int lrow = wave * QW + qb * 32 + lr;
-    const bool ok = lrow < rows;
+  bf16x8 qreg[NDS];
+  {
+    const int lrow = wave * QW + lr;
     const __bf16* src = qg + int64_t(row0 + lrow) * rs + hh * 8;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      if (ok) {
-        qreg[qb][ds] = *reinterpret_cast<const bf16x8*>(src + ds * 16);
-      } else {
-        qreg[qb][ds] = bf16x8{};
-      }
-    }
+    for (int ds = 0; ds < NDS; ++ds)
+      qreg[ds] = lrow < rows ? *reinterpret_cast<const bf16x8*>(src + ds * 16) : bf16x8{};
   }
 
-  f32x16 acc[QB][NDB];
-  float m_run[QB], l_run[QB];
+  f32x16 acc[NDB];
+  float m_run = -__builtin_inff(), l_run = 0.f;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -__builtin_inff();
-    l_run[qb] = 0.f;
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  // ---- DMA addressing.  Instruction i of this wave covers key rows
+  // dma_row[i] .. (RPI rows per instruction); lane -> (row, physical chunk);
+  // it fetches the logical chunk that the swizzle stores there.
+  int dma_row[NI];
+  uint32_t k_goff[NI], v_goff[NI];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x16{};
+  for (int i = 0; i < NI; ++i) {
+    const int q = wave * NI + i;
+    const int r = q * RPI + lane / CH;
+    const int pc = lane % CH;
+    dma_row[i] = r;
+    k_goff[i] = uint32_t(r * rsb + ((pc ^ (r % CH)) * 16));
+    v_goff[i] = uint32_t(r * rsb + ((pc ^ (2 * (r & 3))) * 16));
   }
 
-  // ---- global -> register staging of one K/V step.  Per-thread byte
-  // offsets relative to the tile's first key are fixed; a tile that lies
-  // inside one key interval is addressed from a scalar base.
-  const int64_t rsb = rs * 2;  // token stride in bytes
-  constexpr int KROWS = 256 / DC;  // key rows covered by one K chunk pass
-  const int ktid = tid - K0;
-  const bool k_loader = ktid >= 0 && ktid < 256;
-  const int k_r0 = ktid / DC;
-  const uint32_t k_off = uint32_t(k_r0 * rsb + (ktid - k_r0 * DC) * 16);
-  const int v_kq = tid % (KT / 4);
-  const int v_cc = tid / (KT / 4);
-  const uint32_t v_off = uint32_t(v_kq * 4 * rsb + v_cc * 16);
-
-  u32x4 kst[KCH];
-  u32x4 vst[4];
-  // How a step's KT keys are addressed: from one scalar base when they lie
-  // inside one key interval (the common case), else key by key.  K runs two
-  // steps ahead of the softmax and V one step ahead, so each keeps its own
-  // interval cursor.
-  struct Plan {
-    bool fast;
-    int64_t base;  // byte offset of the step's first key (fast path)
-  };
-  auto plan = [&](int step, int& iv) -> Plan {
+  // Addresses of one step's keys: a scalar base when the step lies inside
+  // one key interval, else key by key (rows past the end of the key list are
+  // clamped to its last key and masked out of the softmax).
+  int ivk = 0, ivv = 0;
+  auto issue = [&](int step, auto stage_c, bool is_k) {
+    constexpr int st = decltype(stage_c)::value;
+    int& iv = is_k ? ivk : ivv;
+    const char* gbase = is_k ? kg : vg;
+    char* lbase = (is_k ? Ks : Vs) + st * TILE;
     const int j0 = step * KT;
     while (iv + 1 < d.n_iv && j0 >= d.iv_start[iv + 1]) ++iv;
     const int iv_end = (iv + 1 < d.n_iv) ? d.iv_start[iv + 1] : n_keys;
-    return Plan{j0 + KT <= iv_end, int64_t(j0 + d.iv_delta[iv]) * rsb};
-  };
-  auto load_k = [&](int step, const Plan& pl) {
-    if (!k_loader) return;
-    if (pl.fast) {
+    if (j0 + KT <= iv_end) {
+      const char* base = gbase + int64_t(j0 + d.iv_delta[iv]) * rsb;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c)
-        kst[c] = *reinterpret_cast<const u32x4*>(kg + (pl.base + c * KROWS * rsb) + k_off);
+      for (int i = 0; i < NI; ++i)
+        __builtin_amdgcn_global_load_lds(base + (is_k ? k_goff[i] : v_goff[i]),
+                                         VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
     } else {
-      const int j0 = step * KT;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) {
-        const int j = j0 + c * KROWS + k_r0;
-        if (j < n_keys) {
-          kst[c] = *reinterpret_cast<const u32x4*>(kg + int64_t(vtoken(d, j)) * rsb +
-                                                    (k_off - uint32_t(k_r0 * rsb)));
-        } else {
-          kst[c] = u32x4{0u, 0u, 0u, 0u};
-        }
+      for (int i = 0; i < NI; ++i) {
+        const int j = min(j0 + dma_row[i], n_keys - 1);
+        const uint32_t goff = (is_k ? k_goff[i] : v_goff[i]) - uint32_t(dma_row[i] * rsb);
+        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(d, j)) * rsb + goff,
+                                         VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
       }
     }
   };
-  auto load_v = [&](int step, const Plan& pl) {
-    if (tid >= VITEMS) return;
-    if (pl.fast) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vst[i] = *reinterpret_cast<const u32x4*>(vg + (pl.base + i * rsb) + v_off);
-    } else {
-      const int j0 = step * KT;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + v_kq * 4 + i;
-        if (j < n_keys) {
-          vst[i] = *reinterpret_cast<const u32x4*>(vg + int64_t(vtoken(d, j)) * rsb + v_cc * 16);
-        } else {
-          vst[i] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    }
+  auto issue_step = [&](int step, auto stage_c) {
+    issue(step, stage_c, true);
+    issue(step, stage_c, false);
   };
-  auto store_k = [&](int buf) {
-    if (!k_loader) return;
-    __bf16* ks = Ks + buf * KBUF;
+
+  // ---- LDS read offsets (bytes, relative to a stage).
+  // K A-operand for k-step ds: row lr (+32 kb), logical chunk 2 ds + hh.
+  uint32_t k_roff[NDS];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int u = c * 256 + ktid;
-      const int kr = u / DC;
-      const int cc = u - kr * DC;
-      *reinterpret_cast<u32x4*>(&ks[kr * KP + cc * 8]) = kst[c];
-    }
-  };
-  auto store_v = [&](int buf) {
-    if (tid >= VITEMS) return;
-    __bf16* vt = Vt + buf * VBUF;
-    // 4 keys x 8 d in registers -> 8 rows of V^T, 4 keys (8 bytes) each.
-    const int pos = vt_pos(v_kq * 4);
+  for (int ds = 0; ds < NDS; ++ds) k_roff[ds] = uint32_t(lr * RB + (((2 * ds + hh) ^ (lr % CH)) * 16));
+  // V^T A-operand (tr reads) for d block db: 16-lane group g, lane i in it:
+  // key 4 hh + i/4 (+ 32 kb + 16 half + 8 r), columns 32 db + 16 (g % 2) + 4 (i % 4).
+  uint32_t v_roff[NDB];
+  {
+    const int g = lane >> 4, i = lane & 15;
+    const int key = 4 * hh + (i >> 2);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t a0 = vst[0][m], a1 = vst[1][m], a2 = vst[2][m], a3 = vst[3][m];
-      const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-      const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-      *reinterpret_cast<u32x2*>(&vt[(v_cc * 8 + 2 * m) * VP + pos]) = even;
-      *reinterpret_cast<u32x2*>(&vt[(v_cc * 8 + 2 * m + 1) * VP + pos]) = odd;
+    for (int db = 0; db < NDB; ++db) {
+      const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
+      const int chunk = (col >> 3) ^ (2 * (key & 3));
+      v_roff[db] = uint32_t(key * RB + chunk * 16 + (col & 7) * 2);
     }
-  };
+  }
 
   const float c = p.score_scale_log2;
   const int nsteps = (n_keys + KT - 1) / KT;
   const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // S^T = K Q^T for the KT keys in K buffer `buf`.
-  auto qk = [&](int buf, f32x16 (&s)[NKB][QB]) {
-    const __bf16* ks = Ks + buf * KBUF;
+  // S^T = K Q^T for the KT keys in K stage `st`.
+  auto qk = [&](auto stage_c, f32x16 (&s)[NKB]) {
+    constexpr int st = decltype(stage_c)::value;
+    const char* ks = Ks + st * TILE;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[(kb * 32 + lr) * KP + ds * 16 + hh * 8]);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[qb][ds], s[kb][qb], 0, 0, 0);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * RB + k_roff[ds]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], s[kb], 0, 0, 0);
       }
     }
   };
 
-  // One step of the software pipeline: softmax of step `step` (scores in
-  // s_cur) and P V with V buffer step&1, while the MFMA units compute the
-  // scores of step+1 into s_next from K buffer (step+1)&1.  On the last step
-  // that product reads a stale buffer and is discarded.
-  int ivk = 0, ivv = 0;
-  auto body = [&](int step, f32x16 (&s_cur)[NKB][QB], f32x16 (&s_next)[NKB][QB]) {
-    const int buf = step & 1;
-    const bool has1 = step + 1 < nsteps;
-    const bool has2 = step + 2 < nsteps;
-    if (has2) load_k(step + 2, plan(step + 2, ivk));
-    if (has1) load_v(step + 1, plan(step + 1, ivv));
+  // Wait for this wave's DMA of the stages the next step reads, then a
+  // workgroup barrier (which also orders the LDS reads around it).
+  auto sync_step = [&](int step) {
+    // issued so far: steps 0 .. min(step + 3, nsteps - 1); the next step
+    // reads K of step+2 and V of step+1, so the newest batch (step+3) and
+    // the V half of batch step+2 may still be in flight.
+    if (step + 3 < nsteps) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    __syncthreads();
+  };
+
+  // One step of the software pipeline, with stage = step % 4: softmax of
+  // step `step` (scores in s_cur) and P V from V stage `stage`, while the
+  // MFMA units compute the scores of step+1 from K stage (stage+1)%4 into
+  // s_next (discarded on the last step).  Then refill the stage freed by the
+  // previous step with step+3 and synchronise.
+  auto body = [&](int step, auto stage_c, f32x16 (&s_cur)[NKB], f32x16 (&s_next)[NKB]) {
+    constexpr int st = decltype(stage_c)::value;
+    if (step + 3 < nsteps) issue_step(step + 3, IC<(st + 3) % 4>{});
 
     // mask the tail of the key list
     const int j0 = step * KT;
@@ -279,42 +265,36 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j >= n_keys) {
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s_cur[kb][qb][r] = -__builtin_inff();
-          }
+          if (j >= n_keys) s_cur[kb][r] = -__builtin_inff();
         }
     }
     // running maximum; rescale only when it grew by more than the slack
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(s_cur[0][qb][0], s_cur[0][qb][1]);
+    {
+      float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2)
-          mx = fmaxf(mx, fmaxf(s_cur[kb][qb][r], s_cur[kb][qb][r + 1]));
+        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[kb][r], s_cur[kb][r + 1]));
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-      if (__any(mx > m_run[qb] + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run[qb], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        l_run[qb] *= alpha;
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[qb][db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
     }
 
     // scores of the next step (independent of the softmax below)
-    qk(buf ^ 1, s_next);
+    qk(IC<(st + 1) % 4>{}, s_next);
 
     // P = exp2(S c - m), packed to bf16; row sums over the rounded weights
-    bf16x8 pk[QB][NKB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mneg = -m_run[qb];
+    bf16x8 pk[NKB][2];
+    {
+      const float mneg = -m_run;
       float lsum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -323,92 +303,102 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
           bf16x8 v8;
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][qb][half * 8 + e], c, mneg)));
-          pk[qb][kb][half] = v8;
+            v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][half * 8 + e], c, mneg)));
+          pk[kb][half] = v8;
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 0, 1), kOnes2, lsum, false);
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 2, 3), kOnes2, lsum, false);
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 4, 5), kOnes2, lsum, false);
           lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 6, 7), kOnes2, lsum, false);
         }
       }
-      l_run[qb] += lsum;
+      l_run += lsum;
     }
 
-    // O^T += V^T P^T
-    const __bf16* vt = Vt + buf * VBUF;
+    // O^T += V^T P^T (V^T fragments by transposing LDS reads)
+    const char* vs = Vs + st * TILE;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt[(db * 32 + lr) * VP + kb * 32 + half * 16 + hh * 8]);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            acc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[qb][kb][half], acc[qb][db], 0, 0, 0);
+          const char* base = vs + (kb * 32 + half * 16) * RB + v_roff[db];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(base));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(base + 8 * RB));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb][half], acc[db], 0, 0, 0);
         }
       }
     }
-
-    // K of step+2 replaces K of step (read one step ago, before the last
-    // barrier); V of step+1 replaces V of step-1.
-    if (has2) store_k(buf);
-    if (has1) store_v(buf ^ 1);
-    __syncthreads();
+    sync_step(step);
   };
 
-  // prologue: K of steps 0 and 1, V of step 0, scores of step 0
-  load_k(0, plan(0, ivk));
-  load_v(0, plan(0, ivv));
-  store_k(0);
-  store_v(0);
-  if (nsteps > 1) {
-    load_k(1, plan(1, ivk));
-    store_k(1);
+  // prologue: steps 0..2 in flight, scores of step 0
+  issue_step(0, IC<0>{});
+  if (nsteps > 1) issue_step(1, IC<1>{});
+  if (nsteps > 2) issue_step(2, IC<2>{});
+  // step 0's K must have landed: batches 1 and 2 may still be in flight
+  if (nsteps > 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NI));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
   __syncthreads();
-  f32x16 sA[NKB][QB], sB[NKB][QB];
-  qk(0, sA);
+  f32x16 sA[NKB], sB[NKB];
+  qk(IC<0>{}, sA);
+  // step 0 also needs V of step 0 and K of step 1 (batch 0 V half, batch 1)
+  if (nsteps > 2) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  __syncthreads();
   for (int step = 0;;) {
-    body(step, sA, sB);
+    body(step, IC<0>{}, sA, sB);
     if (++step >= nsteps) break;
-    body(step, sB, sA);
+    body(step, IC<1>{}, sB, sA);
+    if (++step >= nsteps) break;
+    body(step, IC<2>{}, sA, sB);
+    if (++step >= nsteps) break;
+    body(step, IC<3>{}, sB, sA);
     if (++step >= nsteps) break;
   }
 
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
   __bf16* og = static_cast<__bf16*>(p.out) + bh_off;
+  const int lrow = wave * QW + lr;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (lrow < rows) {
+    const int row = row0 + lrow;
+    float scale = 1.0f / l_tot;
+    if (p.gate != nullptr) {
+      const float g = p.gate[(int64_t(b) * p.S + row) * p.H + h];
+      scale *= 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
+    }
+    __bf16* dst = og + int64_t(row) * rs;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int lrow = wave * QW + qb * 32 + lr;
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    if (lrow < rows) {
-      const int row = row0 + lrow;
-      float scale = 1.0f / l_tot;
-      if (p.gate != nullptr) {
-        const float g = p.gate[(int64_t(b) * p.S + row) * p.H + h];
-        scale *= 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
-      }
-      __bf16* dst = og + int64_t(row) * rs;
+    for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 o4;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 o4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[qb][db][g4 * 4 + r] * scale);
-          *reinterpret_cast<bf16x4*>(dst + db * 32 + g4 * 8 + hh * 4) = o4;
-        }
-      }
-      if (p.lse != nullptr && hh == 0) {
-        p.lse[(int64_t(b) * p.H + h) * p.S + row] = (m_run[qb] + __log2f(l_tot)) * kLn2;
+        for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[db][g4 * 4 + r] * scale);
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + g4 * 8 + hh * 4) = o4;
       }
     }
+    if (p.lse != nullptr && hh == 0) {
+      p.lse[(int64_t(b) * p.H + h) * p.S + row] = (m_run + __log2f(l_tot)) * kLn2;
+    }
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Waves per workgroup of the bf16 kernel: each wave owns 32 query rows.
+// The bf16 kernel: 8 waves x 32 query rows per workgroup, 64 keys per step,
+// 4-stage LDS ring.
 constexpr int kWaves = 8;
+constexpr int kStages = 4;
 
 int kernel_tile_m(int head_dim, int dtype) {
   (void)head_dim;
@@ -422,9 +412,9 @@ int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype != 0) return int(hipErrorInvalidValue);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, 1, kWaves>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages>), grid, block, 0, st, p);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, 1, kWaves>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
