@@ -67,6 +67,16 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
 
 #define VDN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// Workgroup barrier that orders LDS accesses for the compiler but makes no
+// wave wait for its outstanding vector-memory operations (LDS DMA included);
+// callers wait on vmcnt themselves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xF00);  // lgkmcnt(0): LDS ops issued so far are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // K and V stream through a ring of NS LDS stages filled by
@@ -76,8 +86,8 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // distinct banks:
 //   K: chunk c of key row r is stored at chunk c ^ (r % (D/8)) -- the 32 rows
 //      of a QK^T A-operand read are spread over all chunks;
-//   V: chunk c of key row r is stored at chunk c ^ 2(r % 4) -- the four rows of
-//      a ds_read_b64_tr_b16 land on different 32-byte bank groups.
+//   V: chunk c of key row r is stored at chunk c ^ 4(r % 4) -- the four rows
+//      read by 32 lanes of a ds_read_b64_tr_b16 land on different banks.
 // V^T fragments come from two ds_read_b64_tr_b16 per MFMA: in each group of
 // 16 lanes, lane i receives element (i % 4) of the 8-byte blocks addressed by
 // lanes 4e + i/4 (e = 0..3), so if those lanes point at keys k+e, columns
@@ -98,9 +108,29 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   constexpr int NKB = KT / 32;    // 32-key blocks per step
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
   static_assert(NS == 4, "the main loop is unrolled for a 4-stage ring");
+  // V row swizzle: whole groups of four 16-byte chunks move with key % 4, so
+  // the 32 lanes of a transposing read (4 keys x 32 columns) cover all banks.
+  auto vswz = [](int r) { return (4 * (r & 3)) % CH; };
 
-  __shared__ __attribute__((aligned(1024))) char Ks[NS * TILE];
-  __shared__ __attribute__((aligned(1024))) char Vs[NS * TILE];
+  // One array per stage and tensor, so that alias analysis can tell a DMA
+  // into one stage from reads of another and the compiler's own waits on
+  // the DMA stay precise.
+  __shared__ __attribute__((aligned(1024))) char Ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) char Ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) char Ks2[TILE];
+  __shared__ __attribute__((aligned(1024))) char Ks3[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs1[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs2[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs3[TILE];
+  auto kstage = [&](auto stage_c) -> char* {
+    constexpr int st = decltype(stage_c)::value;
+    return st == 0 ? Ks0 : st == 1 ? Ks1 : st == 2 ? Ks2 : Ks3;
+  };
+  auto vstage = [&](auto stage_c) -> char* {
+    constexpr int st = decltype(stage_c)::value;
+    return st == 0 ? Vs0 : st == 1 ? Vs1 : st == 2 ? Vs2 : Vs3;
+  };
 
   // ---- which tile: XCD-aware remap so that consecutive tiles of one
   // (sample, head) land on the same XCD (workgroups are dealt round-robin
@@ -159,7 +189,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     const int pc = lane % CH;
     dma_row[i] = r;
     k_goff[i] = uint32_t(r * rsb + ((pc ^ (r % CH)) * 16));
-    v_goff[i] = uint32_t(r * rsb + ((pc ^ (2 * (r & 3))) * 16));
+    v_goff[i] = uint32_t(r * rsb + ((pc ^ vswz(r)) * 16));
   }
 
   // Addresses of one step's keys: a scalar base when the step lies inside
@@ -167,10 +197,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // clamped to its last key and masked out of the softmax).
   int ivk = 0, ivv = 0;
   auto issue = [&](int step, auto stage_c, bool is_k) {
-    constexpr int st = decltype(stage_c)::value;
     int& iv = is_k ? ivk : ivv;
     const char* gbase = is_k ? kg : vg;
-    char* lbase = (is_k ? Ks : Vs) + st * TILE;
+    char* lbase = is_k ? kstage(stage_c) : vstage(stage_c);
     const int j0 = step * KT;
     while (iv + 1 < d.n_iv && j0 >= d.iv_start[iv + 1]) ++iv;
     const int iv_end = (iv + 1 < d.n_iv) ? d.iv_start[iv + 1] : n_keys;
@@ -209,7 +238,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
-      const int chunk = (col >> 3) ^ (2 * (key & 3));
+      const int chunk = (col >> 3) ^ vswz(key);
       v_roff[db] = uint32_t(key * RB + chunk * 16 + (col & 7) * 2);
     }
   }
@@ -220,8 +249,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 
   // S^T = K Q^T for the KT keys in K stage `st`.
   auto qk = [&](auto stage_c, f32x16 (&s)[NKB]) {
-    constexpr int st = decltype(stage_c)::value;
-    const char* ks = Ks + st * TILE;
+    const char* ks = kstage(stage_c);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
@@ -235,17 +263,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   };
 
   // Wait for this wave's DMA of the stages the next step reads, then a
-  // workgroup barrier (which also orders the LDS reads around it).
-  auto sync_step = [&](int step) {
-    // issued so far: steps 0 .. min(step + 3, nsteps - 1); the next step
-    // reads K of step+2 and V of step+1, so the newest batch (step+3) and
-    // the V half of batch step+2 may still be in flight.
-    if (step + 3 < nsteps) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    __syncthreads();
+  // workgroup barrier.  The barrier is a bare s_barrier between compiler
+  // memory barriers: a workgroup fence would also wait for the DMA still in
+  // flight for later steps.
+  // Every step issues exactly one batch (K then V of step+3; past the end
+  // of the key list a harmless re-fetch of the last key into the free
+  // stage), so vmcnt arithmetic is the same on every step.  The next step
+  // reads K of step+2 and V of step+1: only V of step+2 and the batch of
+  // step+3 may still be in flight.
+  auto sync_step = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
+    lds_barrier();
   };
 
   // One step of the software pipeline, with stage = step % 4: softmax of
@@ -255,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // previous step with step+3 and synchronise.
   auto body = [&](int step, auto stage_c, f32x16 (&s_cur)[NKB], f32x16 (&s_next)[NKB]) {
     constexpr int st = decltype(stage_c)::value;
-    if (step + 3 < nsteps) issue_step(step + 3, IC<(st + 3) % 4>{});
+    issue_step(step + 3, IC<(st + 3) % 4>{});
 
     // mask the tail of the key list
     const int j0 = step * KT;
@@ -315,7 +343,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     }
 
     // O^T += V^T P^T (V^T fragments by transposing LDS reads)
-    const char* vs = Vs + st * TILE;
+    const char* vs = vstage(stage_c);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -332,29 +360,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
         }
       }
     }
-    sync_step(step);
+    sync_step();
   };
 
   // prologue: steps 0..2 in flight, scores of step 0
   issue_step(0, IC<0>{});
-  if (nsteps > 1) issue_step(1, IC<1>{});
-  if (nsteps > 2) issue_step(2, IC<2>{});
-  // step 0's K must have landed: batches 1 and 2 may still be in flight
-  if (nsteps > 2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * NI));
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  }
-  __syncthreads();
+  issue_step(1, IC<1>{});
+  issue_step(2, IC<2>{});
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * NI));  // K of step 0 has landed
+  lds_barrier();
   f32x16 sA[NKB], sB[NKB];
   qk(IC<0>{}, sA);
-  // step 0 also needs V of step 0 and K of step 1 (batch 0 V half, batch 1)
-  if (nsteps > 2) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));  // V of step 0, K of step 1
+  lds_barrier();
   for (int step = 0;;) {
     body(step, IC<0>{}, sA, sB);
     if (++step >= nsteps) break;
