@@ -41,20 +41,57 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
+[[maybe_unused]] constexpr float kLog2e = 1.4426950408889634f;
+[[maybe_unused]] constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ int vtoken(const QBlockDesc& d, int j) {
-  int t = j + d.iv_delta[0];
-  if (d.n_iv > 1 && j >= d.iv_start[1]) t = j + d.iv_delta[1];
-  if (d.n_iv > 2 && j >= d.iv_start[2]) t = j + d.iv_delta[2];
-  return t;
+// A query block's key list in registers: virtual key j in [start_i,
+// start_{i+1}) is token j + delta_i; unused intervals start at n_keys.
+struct KeyList {
+  int n_keys;
+  int start1, start2;
+  int delta0, delta1, delta2;
+};
+
+__device__ __forceinline__ KeyList load_key_list(const QBlockDesc& d) {
+  KeyList k;
+  k.n_keys = __builtin_amdgcn_readfirstlane(d.n_keys);
+  k.start1 = __builtin_amdgcn_readfirstlane(d.n_iv > 1 ? d.iv_start[1] : d.n_keys);
+  k.start2 = __builtin_amdgcn_readfirstlane(d.n_iv > 2 ? d.iv_start[2] : d.n_keys);
+  k.delta0 = __builtin_amdgcn_readfirstlane(d.iv_delta[0]);
+  k.delta1 = __builtin_amdgcn_readfirstlane(d.n_iv > 1 ? d.iv_delta[1] : 0);
+  k.delta2 = __builtin_amdgcn_readfirstlane(d.n_iv > 2 ? d.iv_delta[2] : 0);
+  return k;
+}
+// Maximum / sum of a value over lanes l and l^32 (the two halves of a wave
+// hold the two halves of one query's keys), with the gfx950 cross-half swap:
+// v_permlane32_swap a, b trades lanes 32..63 of a with lanes 0..31 of b, so
+// with a = b = x every lane then holds x[l % 32] in a and x[l % 32 + 32] in b.
+// Written as inline asm with both registers read-write: the compiler's
+// builtin for it drops its second result.  The s_nop pads cover the
+// VALU-write/permlane-read hazard on either side (no memory is touched).
+__device__ __forceinline__ void xhalf_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float xhalf_max(float x) {
+  float a = x, b = x;
+  xhalf_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  float a = x, b = x;
+  xhalf_swap(a, b);
+  return a + b;
+}
+
+// Token of virtual key j (0 <= j < n_keys).
+__device__ __forceinline__ int vtoken(const KeyList& k, int j) {
+  return j + (j >= k.start2 ? k.delta2 : j >= k.start1 ? k.delta1 : k.delta0);
 }
 
 // Online-softmax reference point may lag the running maximum by up to 2^8 in
 // the base-2 domain: P then stays below 256, exact in bf16 up to rounding,
 // and the accumulator rescale is skipped unless the maximum grows by more.
-constexpr float kRescaleSlack = 8.0f;
+[[maybe_unused]] constexpr float kRescaleSlack = 8.0f;
 
 template <int N>
 using IC = std::integral_constant<int, N>;
@@ -144,10 +181,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   const int h = bh - b * p.H;
   int bi = 0;
   while (bi + 1 < p.n_qblocks && p.blk[bi + 1].tile_prefix <= rank) ++bi;
-  const QBlockDesc& d = p.blk[bi];
-  const int row0 = d.row_lo + (rank - d.tile_prefix) * M;
-  const int rows = min(M, d.row_lo + d.rows - row0);
-  const int n_keys = d.n_keys;
+  // The block's descriptor, copied once into wave-uniform registers (reading
+  // the kernel-argument table with a runtime index inside the loop would be a
+  // vector-memory load, and its wait would also drain the DMA in flight).
+  const KeyList kl = load_key_list(p.blk[bi]);
+  const int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
+  const int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  const int n_keys = kl.n_keys;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -195,16 +235,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // Addresses of one step's keys: a scalar base when the step lies inside
   // one key interval, else key by key (rows past the end of the key list are
   // clamped to its last key and masked out of the softmax).
-  int ivk = 0, ivv = 0;
   auto issue = [&](int step, auto stage_c, bool is_k) {
-    int& iv = is_k ? ivk : ivv;
     const char* gbase = is_k ? kg : vg;
     char* lbase = is_k ? kstage(stage_c) : vstage(stage_c);
     const int j0 = step * KT;
-    while (iv + 1 < d.n_iv && j0 >= d.iv_start[iv + 1]) ++iv;
-    const int iv_end = (iv + 1 < d.n_iv) ? d.iv_start[iv + 1] : n_keys;
+    // interval holding j0, its end and offset (scalar selects)
+    const int iv_end = j0 >= kl.start2 ? n_keys : j0 >= kl.start1 ? kl.start2 : kl.start1;
+    const int delta = j0 >= kl.start2 ? kl.delta2 : j0 >= kl.start1 ? kl.delta1 : kl.delta0;
     if (j0 + KT <= iv_end) {
-      const char* base = gbase + int64_t(j0 + d.iv_delta[iv]) * rsb;
+      const char* base = gbase + int64_t(j0 + delta) * rsb;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         __builtin_amdgcn_global_load_lds(base + (is_k ? k_goff[i] : v_goff[i]),
@@ -214,7 +253,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       for (int i = 0; i < NI; ++i) {
         const int j = min(j0 + dma_row[i], n_keys - 1);
         const uint32_t goff = (is_k ? k_goff[i] : v_goff[i]) - uint32_t(dma_row[i] * rsb);
-        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(d, j)) * rsb + goff,
+        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(kl, j)) * rsb + goff,
                                          VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
       }
     }
@@ -303,7 +342,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[kb][r], s_cur[kb][r + 1]));
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      mx = xhalf_max(mx) * c;
       if (__any(mx > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -387,7 +426,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
   __bf16* og = static_cast<__bf16*>(p.out) + bh_off;
   const int lrow = wave * QW + lr;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = xhalf_sum(l_run);
   if (lrow < rows) {
     const int row = row0 + lrow;
     float scale = 1.0f / l_tot;
