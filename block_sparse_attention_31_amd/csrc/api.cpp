@@ -140,6 +140,8 @@ int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float*
     return fail(VDN_ERR_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
   if (dtype == VDN_FP8_E4M3 && qkv_scales == nullptr)
     return fail(VDN_ERR_UNSUPPORTED, "fp8 inputs need qkv_scales");
+  if (dtype == VDN_FP8_E4M3 && head_dim != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "fp8 inputs need head_dim 128");
   if (dtype == VDN_BF16 && qkv_scales != nullptr)
     return fail(VDN_ERR_INVALID_ARG, "qkv_scales must be NULL for bf16 inputs");
   if (!std::isfinite(softmax_scale))

@@ -1,0 +1,95 @@
+// Device helpers shared by the forward kernels (bf16 and fp8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
+
+#include "fwd_params.hpp"
+
+namespace vdn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+[[maybe_unused]] constexpr float kLog2e = 1.4426950408889634f;
+[[maybe_unused]] constexpr float kLn2 = 0.6931471805599453f;
+
+// A query block's key list in registers: virtual key j in [start_i,
+// start_{i+1}) is token j + delta_i; unused intervals start at n_keys.
+struct KeyList {
+  int n_keys;
+  int start1, start2;
+  int delta0, delta1, delta2;
+};
+
+__device__ __forceinline__ KeyList load_key_list(const QBlockDesc& d) {
+  KeyList k;
+  k.n_keys = __builtin_amdgcn_readfirstlane(d.n_keys);
+  k.start1 = __builtin_amdgcn_readfirstlane(d.n_iv > 1 ? d.iv_start[1] : d.n_keys);
+  k.start2 = __builtin_amdgcn_readfirstlane(d.n_iv > 2 ? d.iv_start[2] : d.n_keys);
+  k.delta0 = __builtin_amdgcn_readfirstlane(d.iv_delta[0]);
+  k.delta1 = __builtin_amdgcn_readfirstlane(d.n_iv > 1 ? d.iv_delta[1] : 0);
+  k.delta2 = __builtin_amdgcn_readfirstlane(d.n_iv > 2 ? d.iv_delta[2] : 0);
+  return k;
+}
+// Maximum / sum of a value over lanes l and l^32 (the two halves of a wave
+// hold the two halves of one query's keys), with the gfx950 cross-half swap:
+// v_permlane32_swap a, b trades lanes 32..63 of a with lanes 0..31 of b, so
+// with a = b = x every lane then holds x[l % 32] in a and x[l % 32 + 32] in b.
+// Written as inline asm with both registers read-write: the compiler's
+// builtin for it drops its second result.  The s_nop pads cover the
+// VALU-write/permlane-read hazard on either side (no memory is touched).
+__device__ __forceinline__ void xhalf_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float xhalf_max(float x) {
+  float a = x, b = x;
+  xhalf_swap(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  float a = x, b = x;
+  xhalf_swap(a, b);
+  return a + b;
+}
+
+// Token of virtual key j (0 <= j < n_keys).
+__device__ __forceinline__ int vtoken(const KeyList& k, int j) {
+  return j + (j >= k.start2 ? k.delta2 : j >= k.start1 ? k.delta1 : k.delta0);
+}
+
+// Online-softmax reference point may lag the running maximum by up to 2^8 in
+// the base-2 domain: P then stays below 256, exact in bf16 up to rounding,
+// and the accumulator rescale is skipped unless the maximum grows by more.
+[[maybe_unused]] constexpr float kRescaleSlack = 8.0f;
+
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);
+}
+
+#define VDN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Workgroup barrier that orders LDS accesses for the compiler but makes no
+// wave wait for its outstanding vector-memory operations (LDS DMA included);
+// callers wait on vmcnt themselves.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F & ~0xF00);  // lgkmcnt(0): LDS ops issued so far are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+}  // namespace vdn

@@ -44,4 +44,7 @@ int kernel_tile_m(int head_dim, int dtype);
 // hipSuccess or the HIP error code.
 int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream);
 
+// fp8 (e4m3) variant, head_dim 128 only.
+int launch_fwd_fp8(const FwdParams& p, int head_dim, void* stream);
+
 }  // namespace vdn

@@ -53,7 +53,8 @@ typedef enum {
   VDN_ERR_INVALID_ARG = -1, /* non-positive size, negative n_text, NULL pointer,
                                or output aliasing an input                      */
   VDN_ERR_UNSUPPORTED = -2, /* head_dim not in {64,128}, unknown dtype, fp8
-                               without scales, too many query blocks            */
+                               without scales or with head_dim != 128, too many
+                               query blocks                                     */
   VDN_ERR_ALIGNMENT = -3,   /* q/k/v/out not 16-byte aligned, gate/lse/scales
                                not 4-byte aligned                               */
   VDN_ERR_OVERFLOW = -4,    /* S or a tensor's element count does not fit the
@@ -75,7 +76,8 @@ typedef enum {
  *             frames (>=1), tokens per frame (>=1), text tokens (>=0),
  *             frames per block (>=1; >= F selects full attention).
  *   heads, head_dim, dtype
- *             heads (>=1); head_dim 64 or 128; VDN_BF16 or VDN_FP8_E4M3.
+ *             heads (>=1); head_dim 64 or 128 (fp8: 128 only); VDN_BF16 or
+ *             VDN_FP8_E4M3.
  *   batch     samples (>=1).
  *   qkv_scales device fp32 [3][heads] (q, k, v scale of each head) for fp8:
  *             the real value of a code c of head h is c * scale[h].

@@ -136,6 +136,7 @@ ERROR_CASES = [
     ("head_dim 96", dict(D=96), -2),
     ("head_dim 256", dict(D=256), -2),
     ("dtype 7", dict(dtype=7), -2),
+    ("fp8 head_dim 64", dict(dtype=1, D=64, scales=A + 6 * STEP), -2),
     ("fp8 without scales", dict(dtype=1), -2),
     ("bf16 with scales", dict(scales=A + 6 * STEP), -1),
     ("scale nan", dict(sm=float("nan")), -1),
