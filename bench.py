@@ -26,14 +26,19 @@ METRIC = "effective TFLOP/s + ms/call, 768p-shaped local-window attn; % MFMA pea
 # Dense MFMA peaks of MI355X in TFLOP/s: 256 CUs x 2.4 GHz x 4096 (bf16) or
 # 8192 (fp8) flop per clock per CU; AMD quotes them as 2.5 and 5.0 PFLOP/s.
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
-KERNEL_SOURCES = {"bf16": "fwd_kernel.hip", "fp8": "fwd_fp8_kernel.hip"}
+KERNEL_SOURCES = {"bf16": ["fwd_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"],
+                  "fp8": ["fwd_fp8_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.json")
 
 
 def kernel_source_hash(dtype: str) -> str:
-    path = os.path.join(ROOT, "block_sparse_attention_31_amd", "csrc", KERNEL_SOURCES[dtype])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources the kernel is compiled from (traffic counters are
+    only reported while they describe the kernel as it is)."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[dtype]:
+        with open(os.path.join(ROOT, "block_sparse_attention_31_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def load_traffic(dtype: str, workload: str):
@@ -51,7 +56,6 @@ def load_traffic(dtype: str, workload: str):
 
 def cpu_baseline(w, inp, seconds: float):
     """Time the fp64 oracle on whole heads of sample 0 until `seconds` pass."""
-    import numpy as np
     import torch
 
     import oracle
@@ -95,6 +99,8 @@ def main() -> int:
     ap.add_argument("--workload", default="768p")
     ap.add_argument("--dense-steps", type=int, default=20, help="0 skips the dense run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
+    ap.add_argument("--also", default="768p-fp8",
+                    help="comma-separated extra workloads reported under 'other_workloads' ('' for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -112,33 +118,8 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     binding.lib()  # fail loudly if the HIP library is missing
-    w = synth.WORKLOADS[args.workload]
-    inp = synth.make_inputs(w)
     dev = torch.device("cuda:0")
-    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
-    gate = None if inp["gate"] is None else inp["gate"].to(dev)
-    scales = None if inp["scales"] is None else inp["scales"].to(dev)
-    out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
-
-    def step(bf):
-        binding.vdn_local_attn_fwd(q, k, v, gate, out, w.F, w.T, w.N, bf, qkv_scales=scales,
-                                   stream=stream.cuda_stream)
-
-    def timed(bf, steps, warmup):
-        for _ in range(warmup):
-            step(bf)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(steps):
-            step(bf)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -146,44 +127,89 @@ def main() -> int:
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    ms, wall_ms = timed(w.Bf, args.steps, args.warmup)
-    print(f"[bench] {w.name} sparse: {ms:.4f} ms/step over {args.steps} steps", file=sys.stderr, flush=True)
-    dense_ms = None
-    if args.dense_steps > 0:
-        dense_ms, _ = timed(w.F, args.dense_steps, 2)
-        print(f"[bench] {w.name} dense: {dense_ms:.4f} ms/step", file=sys.stderr, flush=True)
+    def measure(name: str, steps: int, warmup: int, dense_steps: int):
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        gate = None if inp["gate"] is None else inp["gate"].to(dev)
+        scales = None if inp["scales"] is None else inp["scales"].to(dev)
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
 
-    import oracle  # closed-form pair counts only; no oracle compute on this path
+        def step(bf):
+            binding.vdn_local_attn_fwd(q, k, v, gate, out, w.F, w.T, w.N, bf, qkv_scales=scales,
+                                       stream=stream.cuda_stream)
 
-    allowed, _ = oracle.count_pairs(w.F, w.T, w.N, w.Bf)
-    flops = 4.0 * w.D * w.H * w.B * allowed
-    tflops = flops / (ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(w.dtype, w.name)
+        def timed(bf, n_steps, n_warm):
+            for _ in range(n_warm):
+                step(bf)
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t0 = time.perf_counter()
+            e0.record(stream)
+            for _ in range(n_steps):
+                step(bf)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n_steps, (time.perf_counter() - t0) * 1e3 / n_steps
+
+        ms, wall_ms = timed(w.Bf, steps, warmup)
+        print(f"[bench] {w.name} sparse: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
+        dense_ms = None
+        if dense_steps > 0:
+            dense_ms, _ = timed(w.F, dense_steps, 2)
+            print(f"[bench] {w.name} dense: {dense_ms:.4f} ms/step", file=sys.stderr, flush=True)
+        # closed-form count of attended (query, key) pairs, from the library
+        allowed, _ = binding.vdn_local_attn_count_pairs(w.F, w.T, w.N, w.Bf)
+        tflops = 4.0 * w.D * w.H * w.B * allowed / (ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[w.dtype]
+        rec = {
+            "ms_per_step": round(ms, 4),
+            "tflops": round(tflops, 2),
+            "wall_ms_per_step": round(wall_ms, 4),
+            "dtype": w.dtype,
+            "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
+                       "frames": w.F, "tokens_per_frame": w.T, "text_tokens": w.N,
+                       "seq_len": w.S, "block_frames": w.Bf, "gate": w.gate,
+                       "allowed_pairs_per_head": allowed},
+            "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
+            "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 4),
+            "sparse_vs_dense_speedup": None if dense_ms is None else round(dense_ms / ms, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                         "traffic": load_traffic(w.dtype, w.name)},
+        }
+        return w, inp, rec
+
+    w, inp, main_rec = measure(args.workload, args.steps, args.warmup, args.dense_steps)
     result = {
         "metric": METRIC,
-        "value": round(tflops, 2),
+        "value": main_rec["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": main_rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": main_rec["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
-                   "frames": w.F, "tokens_per_frame": w.T, "text_tokens": w.N, "seq_len": w.S,
-                   "block_frames": w.Bf, "gate": w.gate, "allowed_pairs_per_head": allowed},
-        "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
-        "wall_ms_per_step": round(wall_ms, 4),
-        "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 4),
-        "sparse_vs_dense_speedup": None if dense_ms is None else round(dense_ms / ms, 3),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic},
+        "config": main_rec["config"],
+        "pct_of_mfma_peak": main_rec["pct_of_mfma_peak"],
+        "wall_ms_per_step": main_rec["wall_ms_per_step"],
+        "dense_ms_per_step": main_rec["dense_ms_per_step"],
+        "sparse_vs_dense_speedup": main_rec["sparse_vs_dense_speedup"],
+        "roofline": main_rec["roofline"],
     }
+    others = {}
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        _, _, rec = measure(name, max(args.steps // 2, 5), max(args.warmup // 2, 2), 0)
+        others[name] = rec
+    if others:
+        result["other_workloads"] = others
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
