@@ -59,9 +59,25 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return a + b;
 }
 
+// Three-way select on values.  (A conditional over struct members is an
+// lvalue, and the compiler then picks between their addresses, which forces
+// the struct into memory; going through value parameters keeps it in
+// registers.)
+__device__ __forceinline__ int pick3(int j, int s1, int s2, int a0, int a1, int a2) {
+  return j >= s2 ? a2 : (j >= s1 ? a1 : a0);
+}
+
 // Token of virtual key j (0 <= j < n_keys).
 __device__ __forceinline__ int vtoken(const KeyList& k, int j) {
-  return j + (j >= k.start2 ? k.delta2 : j >= k.start1 ? k.delta1 : k.delta0);
+  return j + pick3(j, k.start1, k.start2, k.delta0, k.delta1, k.delta2);
+}
+
+// End (exclusive) and token offset of the interval holding virtual key j.
+__device__ __forceinline__ int interval_end(const KeyList& k, int j) {
+  return pick3(j, k.start1, k.start2, k.start1, k.start2, k.n_keys);
+}
+__device__ __forceinline__ int interval_delta(const KeyList& k, int j) {
+  return pick3(j, k.start1, k.start2, k.delta0, k.delta1, k.delta2);
 }
 
 // Online-softmax reference point may lag the running maximum by up to 2^8 in

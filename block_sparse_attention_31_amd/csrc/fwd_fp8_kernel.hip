@@ -39,7 +39,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // e4m3fn encoding of 1.0 in every byte.
-constexpr int kFp8Ones = 0x38383838;
+[[maybe_unused]] constexpr int kFp8Ones = 0x38383838;
 // log2 of the factor applied to the weights before rounding them to e4m3.
 [[maybe_unused]] constexpr float kFp8PShift = 8.0f;
 
@@ -152,31 +152,42 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
     k_goff[i] = uint32_t(r * rsb + ((pc ^ kswz(r)) * 16));
     v_goff[i] = uint32_t(r * rsb + ((pc ^ vswz(r)) * 16));
   }
-  auto issue = [&](int step, auto stage_c, bool is_k) {
+  // (the tensor is a compile-time tag: choosing between the two offset arrays
+  // at run time would force them out of registers)
+  auto issue = [&](int step, auto stage_c, auto is_k_c) {
+    constexpr bool is_k = decltype(is_k_c)::value != 0;
+    uint32_t goff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (is_k) {
+        goff[i] = k_goff[i];
+      } else {
+        goff[i] = v_goff[i];
+      }
+    }
     const char* gbase = is_k ? kg : vg;
     char* lbase = is_k ? kstage(stage_c) : vstage(stage_c);
     const int j0 = step * KT;
-    const int iv_end = j0 >= kl.start2 ? n_keys : j0 >= kl.start1 ? kl.start2 : kl.start1;
-    const int delta = j0 >= kl.start2 ? kl.delta2 : j0 >= kl.start1 ? kl.delta1 : kl.delta0;
+    const int iv_end = interval_end(kl, j0);
+    const int delta = interval_delta(kl, j0);
     if (j0 + KT <= iv_end) {
       const char* base = gbase + int64_t(j0 + delta) * rsb;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        __builtin_amdgcn_global_load_lds(base + (is_k ? k_goff[i] : v_goff[i]),
+        __builtin_amdgcn_global_load_lds(base + goff[i],
                                          VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int j = min(j0 + dma_row[i], n_keys - 1);
-        const uint32_t goff = (is_k ? k_goff[i] : v_goff[i]) - uint32_t(dma_row[i] * rsb);
-        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(kl, j)) * rsb + goff,
+        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
                                          VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
       }
     }
   };
   auto issue_step = [&](int step, auto stage_c) {
-    issue(step, stage_c, true);
-    issue(step, stage_c, false);
+    issue(step, stage_c, IC<1>{});
+    issue(step, stage_c, IC<0>{});
   };
 
   // ---- LDS read offsets (bytes within a stage)

@@ -45,10 +45,9 @@ namespace vdn {
 // 16 lanes, lane i receives element (i % 4) of the 8-byte blocks addressed by
 // lanes 4e + i/4 (e = 0..3), so if those lanes point at keys k+e, columns
 // d0 + 4(i/4).., lane i holds V[k..k+3][d0 + i]: the MFMA A-operand layout.
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, int KT, bool PIPE>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-  constexpr int KT = 64;          // keys per step
   constexpr int QW = 32;          // query rows per wave
   constexpr int M = NW * QW;      // query rows per workgroup
   constexpr int RB = 2 * D;       // bytes per key row
@@ -60,7 +59,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   constexpr int NDB = D / 32;     // 32-wide d blocks of the output
   constexpr int NKB = KT / 32;    // 32-key blocks per step
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
-  static_assert(NS == 4, "the main loop is unrolled for a 4-stage ring");
+  static_assert(NS == 2 || NS == 4, "the main loop is unrolled for a 2- or 4-stage ring");
+  static_assert(!PIPE || NS == 4, "pipelined scores need K two steps ahead");
   // V row swizzle: whole groups of four 16-byte chunks move with key % 4, so
   // the 32 lanes of a transposing read (4 keys x 32 columns) cover all banks.
   auto vswz = [](int r) { return (4 * (r & 3)) % CH; };
@@ -68,14 +68,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // One array per stage and tensor, so that alias analysis can tell a DMA
   // into one stage from reads of another and the compiler's own waits on
   // the DMA stay precise.
+  constexpr int T2 = NS > 2 ? TILE : 16;  // stages 2 and 3 exist only in the 4-stage ring
   __shared__ __attribute__((aligned(1024))) char Ks0[TILE];
   __shared__ __attribute__((aligned(1024))) char Ks1[TILE];
-  __shared__ __attribute__((aligned(1024))) char Ks2[TILE];
-  __shared__ __attribute__((aligned(1024))) char Ks3[TILE];
+  __shared__ __attribute__((aligned(1024))) char Ks2[T2];
+  __shared__ __attribute__((aligned(1024))) char Ks3[T2];
   __shared__ __attribute__((aligned(1024))) char Vs0[TILE];
   __shared__ __attribute__((aligned(1024))) char Vs1[TILE];
-  __shared__ __attribute__((aligned(1024))) char Vs2[TILE];
-  __shared__ __attribute__((aligned(1024))) char Vs3[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs2[T2];
+  __shared__ __attribute__((aligned(1024))) char Vs3[T2];
   auto kstage = [&](auto stage_c) -> char* {
     constexpr int st = decltype(stage_c)::value;
     return st == 0 ? Ks0 : st == 1 ? Ks1 : st == 2 ? Ks2 : Ks3;
@@ -151,32 +152,43 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // Addresses of one step's keys: a scalar base when the step lies inside
   // one key interval, else key by key (rows past the end of the key list are
   // clamped to its last key and masked out of the softmax).
-  auto issue = [&](int step, auto stage_c, bool is_k) {
+  // (the tensor is a compile-time tag: choosing between the two offset arrays
+  // at run time would force them out of registers)
+  auto issue = [&](int step, auto stage_c, auto is_k_c) {
+    constexpr bool is_k = decltype(is_k_c)::value != 0;
+    uint32_t goff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (is_k) {
+        goff[i] = k_goff[i];
+      } else {
+        goff[i] = v_goff[i];
+      }
+    }
     const char* gbase = is_k ? kg : vg;
     char* lbase = is_k ? kstage(stage_c) : vstage(stage_c);
     const int j0 = step * KT;
     // interval holding j0, its end and offset (scalar selects)
-    const int iv_end = j0 >= kl.start2 ? n_keys : j0 >= kl.start1 ? kl.start2 : kl.start1;
-    const int delta = j0 >= kl.start2 ? kl.delta2 : j0 >= kl.start1 ? kl.delta1 : kl.delta0;
+    const int iv_end = interval_end(kl, j0);
+    const int delta = interval_delta(kl, j0);
     if (j0 + KT <= iv_end) {
       const char* base = gbase + int64_t(j0 + delta) * rsb;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        __builtin_amdgcn_global_load_lds(base + (is_k ? k_goff[i] : v_goff[i]),
+        __builtin_amdgcn_global_load_lds(base + goff[i],
                                          VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int j = min(j0 + dma_row[i], n_keys - 1);
-        const uint32_t goff = (is_k ? k_goff[i] : v_goff[i]) - uint32_t(dma_row[i] * rsb);
-        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(kl, j)) * rsb + goff,
+        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
                                          VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
       }
     }
   };
   auto issue_step = [&](int step, auto stage_c) {
-    issue(step, stage_c, true);
-    issue(step, stage_c, false);
+    issue(step, stage_c, IC<1>{});
+    issue(step, stage_c, IC<0>{});
   };
 
   // ---- LDS read offsets (bytes, relative to a stage).
@@ -227,7 +239,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // reads K of step+2 and V of step+1: only V of step+2 and the batch of
   // step+3 may still be in flight.
   auto sync_step = [&]() {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
+    if constexpr (PIPE) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
+    } else {
+      // the next step reads K and V of step+1: batches step+2 .. step+NS-1
+      // may still be in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
+    }
     lds_barrier();
   };
 
@@ -238,7 +256,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // previous step with step+3 and synchronise.
   auto body = [&](int step, auto stage_c, f32x16 (&s_cur)[NKB], f32x16 (&s_next)[NKB]) {
     constexpr int st = decltype(stage_c)::value;
-    issue_step(step + 3, IC<(st + 3) % 4>{});
+    issue_step(step + NS - 1, IC<(st + NS - 1) % NS>{});
+    if constexpr (!PIPE) qk(stage_c, s_cur);
 
     // mask the tail of the key list
     const int j0 = step * KT;
@@ -272,7 +291,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     }
 
     // scores of the next step (independent of the softmax below)
-    qk(IC<(st + 1) % 4>{}, s_next);
+    if constexpr (PIPE) qk(IC<(st + 1) % NS>{}, s_next);
 
     // P = exp2(S c - m), packed to bf16; row sums over the rounded weights
     bf16x8 pk[NKB][2];
@@ -318,25 +337,32 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     sync_step();
   };
 
-  // prologue: steps 0..2 in flight, scores of step 0
+  // prologue: steps 0 .. NS-2 in flight (pipelined: also the scores of step 0)
   issue_step(0, IC<0>{});
-  issue_step(1, IC<1>{});
-  issue_step(2, IC<2>{});
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * NI));  // K of step 0 has landed
-  lds_barrier();
+  issue_step(1, IC<1 % NS>{});
+  if constexpr (NS > 2) issue_step(2, IC<2 % NS>{});
   f32x16 sA[NKB], sB[NKB];
-  qk(IC<0>{}, sA);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));  // V of step 0, K of step 1
-  lds_barrier();
+  if constexpr (PIPE) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * NI));  // K of step 0 has landed
+    lds_barrier();
+    qk(IC<0>{}, sA);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));  // V of step 0, K of step 1
+    lds_barrier();
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
+    lds_barrier();
+  }
   for (int step = 0;;) {
     body(step, IC<0>{}, sA, sB);
     if (++step >= nsteps) break;
-    body(step, IC<1>{}, sB, sA);
+    body(step, IC<1 % NS>{}, sB, sA);
     if (++step >= nsteps) break;
-    body(step, IC<2>{}, sA, sB);
-    if (++step >= nsteps) break;
-    body(step, IC<3>{}, sB, sA);
-    if (++step >= nsteps) break;
+    if constexpr (NS > 2) {
+      body(step, IC<2 % NS>{}, sA, sB);
+      if (++step >= nsteps) break;
+      body(step, IC<3 % NS>{}, sB, sA);
+      if (++step >= nsteps) break;
+    }
   }
 
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
@@ -368,10 +394,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// The bf16 kernel: 8 waves x 32 query rows per workgroup, 64 keys per step,
-// 4-stage LDS ring.
+// The bf16 kernel: 8 waves x 32 query rows per workgroup, 128 keys per step,
+// 2-stage LDS ring (K and V of step j+1 land while step j computes).  The
+// template also builds 64-key steps over a 4-stage ring with the scores of
+// step j+1 computed under step j's softmax; on the 768p workload that shape
+// measured 3% slower.
+#ifndef VDN_BF16_KT
+#define VDN_BF16_KT 128
+#endif
+#ifndef VDN_BF16_STAGES
+#define VDN_BF16_STAGES 2
+#endif
+#ifndef VDN_BF16_PIPE
+#define VDN_BF16_PIPE 0
+#endif
 constexpr int kWaves = 8;
-constexpr int kStages = 4;
+constexpr int kStages = VDN_BF16_STAGES;
+constexpr int kKeysPerStep = VDN_BF16_KT;
+constexpr bool kPipe = VDN_BF16_PIPE != 0;
 
 int kernel_tile_m(int head_dim, int dtype) {
   (void)head_dim;
@@ -386,9 +426,9 @@ int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
   if (dtype == 1) return launch_fwd_fp8(p, head_dim, stream);
   if (dtype != 0) return int(hipErrorInvalidValue);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kPipe>), grid, block, 0, st, p);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kPipe>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
