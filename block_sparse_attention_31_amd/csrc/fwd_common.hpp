@@ -88,6 +88,27 @@ __device__ __forceinline__ int interval_delta(const KeyList& k, int j) {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
+// Sets the scores of keys past the end of the key list to -inf on a partial
+// last step.  Score register (kb, r) of a 32x32 MFMA result holds key
+// 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 of the step; `lim` (wave-uniform)
+// is the number of valid keys in the step.  The mask is a min with +-inf:
+// (rem - offset - 1/2) is never zero, so its product with +inf is +inf for a
+// valid key and -inf past the end.  Written without compares (each would
+// produce a 64-bit lane mask in scalar registers, which the compiler keeps
+// alive side by side) and without integer bit operations on the scores
+// (which this compiler fuses into wrong three-input bit operations).
+template <int NKB>
+__device__ __forceinline__ void mask_tail(f32x16 (&s)[NKB], int lim, int hh) {
+  const float rem = float(lim - 4 * hh);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float off = float(kb * 32 + 8 * (r >> 2) + (r & 3)) + 0.5f;
+      s[kb][r] = fminf(s[kb][r], (rem - off) * __builtin_inff());
+    }
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 __host__ __device__ constexpr int vmcnt_imm(int n) {
@@ -95,6 +116,38 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
 }
 
 #define VDN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+#ifndef VDN_ASM_DMA
+#define VDN_ASM_DMA 1
+#endif
+
+// LDS DMA, 16 bytes per lane: lane L's 16 bytes at its global address land
+// at LDS byte lds + 16 L (lds wave-uniform).  Two forms: a scalar base plus
+// a 32-bit per-lane offset, and a full per-lane address.
+// Issued through inline asm rather than the compiler's builtin: while a
+// builtin LDS DMA is outstanding (until a joint vmcnt(0) lgkmcnt(0) wait) the
+// compiler turns every wait for an LDS read into lgkmcnt(0), so no LDS read
+// can be in flight while the MFMAs consume earlier ones.  The asm form is
+// invisible to that bookkeeping; the hardware counts the DMA on vmcnt only,
+// and the kernels order the destination with explicit vmcnt waits and
+// barriers.  No VGPR is written by the asm (the data goes to LDS), and the
+// leading s_nop covers the M0 write and the SGPR-base write that precede it.
+__device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, const char* lds) {
+#if VDN_ASM_DMA
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+#else
+  __builtin_amdgcn_global_load_lds(sbase + voff, VDN_LDS(lds), 16, 0, 0);
+#endif
+}
+__device__ __forceinline__ void lds_dma16(const char* gaddr, const char* lds) {
+#if VDN_ASM_DMA
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds)));
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gaddr), "{m0}"(m0) : "memory");
+#else
+  __builtin_amdgcn_global_load_lds(gaddr, VDN_LDS(lds), 16, 0, 0);
+#endif
+}
 
 // Workgroup barrier that orders LDS accesses for the compiler but makes no
 // wave wait for its outstanding vector-memory operations (LDS DMA included);

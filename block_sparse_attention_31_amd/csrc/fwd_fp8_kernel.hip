@@ -177,14 +177,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
       const char* base = gbase + int64_t(j0 + delta) * rsb;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        __builtin_amdgcn_global_load_lds(base + goff[i],
-                                         VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
+        lds_dma16(base, goff[i], lbase + (wave * NI + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int j = min(j0 + dma_row[i], n_keys - 1);
-        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
-                                         VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
+        lds_dma16(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
+                  lbase + (wave * NI + i) * 1024);
       }
     }
   };
@@ -248,15 +247,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
     if constexpr (!PIPE) qk(stage_c, s_cur);
 
     const int j0 = step * KT;
-    if (j0 + KT > n_keys) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j >= n_keys) s_cur[kb][r] = -__builtin_inff();
-        }
-    }
+    if (j0 + KT > n_keys) mask_tail<NKB>(s_cur, n_keys - j0, hh);
     {
       float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
 #pragma unroll

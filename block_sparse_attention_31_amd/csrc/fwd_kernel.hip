@@ -9,26 +9,31 @@
 // ("Gated Fusion Mechanism" on the same page).
 //
 // Work decomposition
-//   One workgroup = 4 waves = one tile of M query rows of one (sample, head,
-//   query block); each wave owns 32*QB query rows.  The key list of the block
-//   is the virtual concatenation of <= 3 token intervals, walked in steps of
-//   KT = 64 keys; only the last step can be partial.
+//   One workgroup = NW waves = one tile of 32*NW query rows of one (sample,
+//   head, query block); each wave owns 32 query rows.  The key list of the
+//   block is the virtual concatenation of <= 3 token intervals, walked in
+//   steps of KT keys; only the last step can be partial.  Default shape: 8
+//   waves (two per SIMD), 128 keys per step, a 2-stage LDS ring.
 //
 // Matrix layout on the MFMA units (v_mfma_f32_32x32x16_bf16)
 //   S^T = K Q^T: A = K rows from LDS, B = Q rows held in registers.  The
 //   32x32 result puts one query per lane column: lane l holds query l%32 and
 //   keys {8g + 4(l/32) + r}, so the row max/sum is an in-lane reduction plus
 //   one exchange with lane l^32.
-//   O^T = V^T P^T: B = P straight from the S^T registers (packed to bf16),
-//   A = V^T read from an LDS copy of V stored transposed, with keys placed so
-//   that the 8 keys a half-wave contributes are contiguous (bits 2 and 3 of
-//   the key index swapped).  The accumulator again has one query per lane,
-//   so the online-softmax rescale is a per-lane scalar multiply.
+//   O^T = V^T P^T: B = P straight from the S^T registers (packed to bf16;
+//   the key order inside the 32-key block only has to agree between A and
+//   B), A = V^T fragments from transposing LDS reads of row-major V.  The
+//   accumulator again has one query per lane, so the online-softmax rescale
+//   is a per-lane scalar multiply.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "fwd_common.hpp"
+
+#ifndef VDN_PIN_QK
+#define VDN_PIN_QK 1
+#endif
 
 namespace vdn {
 
@@ -45,7 +50,7 @@ namespace vdn {
 // 16 lanes, lane i receives element (i % 4) of the 8-byte blocks addressed by
 // lanes 4e + i/4 (e = 0..3), so if those lanes point at keys k+e, columns
 // d0 + 4(i/4).., lane i holds V[k..k+3][d0 + i]: the MFMA A-operand layout.
-template <int D, int NW, int NS, int KT, bool PIPE>
+template <int D, int NW, int NS, int KT, int KPF>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int QW = 32;          // query rows per wave
@@ -60,7 +65,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   constexpr int NKB = KT / 32;    // 32-key blocks per step
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
   static_assert(NS == 2 || NS == 4, "the main loop is unrolled for a 2- or 4-stage ring");
-  static_assert(!PIPE || NS == 4, "pipelined scores need K two steps ahead");
   // V row swizzle: whole groups of four 16-byte chunks move with key % 4, so
   // the 32 lanes of a transposing read (4 keys x 32 columns) cover all banks.
   auto vswz = [](int r) { return (4 * (r & 3)) % CH; };
@@ -175,148 +179,72 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       const char* base = gbase + int64_t(j0 + delta) * rsb;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
-        __builtin_amdgcn_global_load_lds(base + goff[i],
-                                         VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
+        lds_dma16(base, goff[i], lbase + (wave * NI + i) * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int j = min(j0 + dma_row[i], n_keys - 1);
-        __builtin_amdgcn_global_load_lds(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
-                                         VDN_LDS(lbase + (wave * NI + i) * 1024), 16, 0, 0);
+        lds_dma16(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
+                  lbase + (wave * NI + i) * 1024);
       }
     }
   };
-  auto issue_step = [&](int step, auto stage_c) {
-    issue(step, stage_c, IC<1>{});
-    issue(step, stage_c, IC<0>{});
-  };
 
   // ---- LDS read offsets (bytes, relative to a stage).
-  // K A-operand for k-step ds: row lr (+32 kb), logical chunk 2 ds + hh.
-  uint32_t k_roff[NDS];
-#pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) k_roff[ds] = uint32_t(lr * RB + (((2 * ds + hh) ^ (lr % CH)) * 16));
+  // K A-operand for k-step ds: row lr (+32 kb), logical chunk 2 ds + hh,
+  // stored at chunk (2 ds + hh) ^ (lr % CH): bits 5.. of the offset carry
+  // ds, so the offset for ds is k_roff0 ^ (32 ds) (one VALU op per read
+  // instead of a register per k-step).
+  const uint32_t k_roff0 = uint32_t(lr * RB + ((hh ^ (lr % CH)) * 16));
+  auto k_roff = [&](int ds) { return k_roff0 ^ uint32_t(32 * ds); };
   // V^T A-operand (tr reads) for d block db: 16-lane group g, lane i in it:
   // key 4 hh + i/4 (+ 32 kb + 16 half + 8 r), columns 32 db + 16 (g % 2) + 4 (i % 4).
-  uint32_t v_roff[NDB];
+  // db only moves bits 6.. of the offset (chunk bits 2..), which the V
+  // swizzle XORs, so the offset for db is v_roff0 ^ (64 db).
+  uint32_t v_roff0;
   {
     const int g = lane >> 4, i = lane & 15;
     const int key = 4 * hh + (i >> 2);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int col = 32 * db + 16 * (g & 1) + 4 * (i & 3);
-      const int chunk = (col >> 3) ^ vswz(key);
-      v_roff[db] = uint32_t(key * RB + chunk * 16 + (col & 7) * 2);
-    }
+    const int col = 16 * (g & 1) + 4 * (i & 3);
+    const int chunk = (col >> 3) ^ vswz(key);
+    v_roff0 = uint32_t(key * RB + chunk * 16 + (col & 7) * 2);
   }
+  auto v_roff = [&](int db) { return v_roff0 ^ uint32_t(64 * db); };
 
   const float c = p.score_scale_log2;
   const int nsteps = (n_keys + KT - 1) / KT;
   const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // S^T = K Q^T for the KT keys in K stage `st`.
+  // S^T = K Q^T for the KT keys in K stage `stage_c`.  The K fragments run
+  // KPF reads ahead of the MFMAs that consume them (a read issued just
+  // before its MFMA leaves the LDS latency on the critical path).
   auto qk = [&](auto stage_c, f32x16 (&s)[NKB]) {
     const char* ks = kstage(stage_c);
+    constexpr int NF = NDS * NKB;  // fragments (= MFMAs) per step
+    constexpr int PF = KPF < NF ? KPF : NF;
+    auto frag = [&](int f) {
+      return *reinterpret_cast<const bf16x8*>(ks + (f % NKB) * 32 * RB + k_roff(f / NKB));
+    };
+    bf16x8 fr[PF];
+#pragma unroll
+    for (int f = 0; f < PF; ++f) fr[f] = frag(f);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kb * 32 * RB + k_roff[ds]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ds], s[kb], 0, 0, 0);
-      }
+    for (int f = 0; f < NF; ++f) {
+      s[f % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % PF], qreg[f / NKB], s[f % NKB], 0, 0, 0);
+      if (f + PF < NF) fr[f % PF] = frag(f + PF);
+#if VDN_PIN_QK
+      // keep this order: the scheduler would otherwise pull the reads back
+      // next to their MFMAs to save registers
+      __builtin_amdgcn_sched_barrier(0);
+#endif
     }
   };
 
-  // Wait for this wave's DMA of the stages the next step reads, then a
-  // workgroup barrier.  The barrier is a bare s_barrier between compiler
-  // memory barriers: a workgroup fence would also wait for the DMA still in
-  // flight for later steps.
-  // Every step issues exactly one batch (K then V of step+3; past the end
-  // of the key list a harmless re-fetch of the last key into the free
-  // stage), so vmcnt arithmetic is the same on every step.  The next step
-  // reads K of step+2 and V of step+1: only V of step+2 and the batch of
-  // step+3 may still be in flight.
-  auto sync_step = [&]() {
-    if constexpr (PIPE) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
-    } else {
-      // the next step reads K and V of step+1: batches step+2 .. step+NS-1
-      // may still be in flight
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
-    }
-    lds_barrier();
-  };
-
-  // One step of the software pipeline, with stage = step % 4: softmax of
-  // step `step` (scores in s_cur) and P V from V stage `stage`, while the
-  // MFMA units compute the scores of step+1 from K stage (stage+1)%4 into
-  // s_next (discarded on the last step).  Then refill the stage freed by the
-  // previous step with step+3 and synchronise.
-  auto body = [&](int step, auto stage_c, f32x16 (&s_cur)[NKB], f32x16 (&s_next)[NKB]) {
-    constexpr int st = decltype(stage_c)::value;
-    issue_step(step + NS - 1, IC<(st + NS - 1) % NS>{});
-    if constexpr (!PIPE) qk(stage_c, s_cur);
-
-    // mask the tail of the key list
-    const int j0 = step * KT;
-    if (j0 + KT > n_keys) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + kb * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (j >= n_keys) s_cur[kb][r] = -__builtin_inff();
-        }
-    }
-    // running maximum; rescale only when it grew by more than the slack
-    {
-      float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[kb][r], s_cur[kb][r + 1]));
-      mx = xhalf_max(mx) * c;
-      if (__any(mx > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-      }
-    }
-
-    // scores of the next step (independent of the softmax below)
-    if constexpr (PIPE) qk(IC<(st + 1) % NS>{}, s_next);
-
-    // P = exp2(S c - m), packed to bf16; row sums over the rounded weights
-    bf16x8 pk[NKB][2];
-    {
-      const float mneg = -m_run;
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          bf16x8 v8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kb][half * 8 + e], c, mneg)));
-          pk[kb][half] = v8;
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 0, 1), kOnes2, lsum, false);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 2, 3), kOnes2, lsum, false);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 4, 5), kOnes2, lsum, false);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 6, 7), kOnes2, lsum, false);
-        }
-      }
-      l_run += lsum;
-    }
-
-    // O^T += V^T P^T (V^T fragments by transposing LDS reads)
+  // O^T += V^T P^T for the KT keys in V stage `stage_c` (V^T fragments by
+  // transposing LDS reads).
+  auto pv = [&](auto stage_c, const bf16x8 (&pk)[NKB][2]) {
     const char* vs = vstage(stage_c);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -324,7 +252,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       for (int half = 0; half < 2; ++half) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const char* base = vs + (kb * 32 + half * 16) * RB + v_roff[db];
+          const char* base = vs + (kb * 32 + half * 16) * RB + v_roff(db);
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) s16x4*)(base));
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -334,36 +262,99 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
         }
       }
     }
-    sync_step();
   };
 
-  // prologue: steps 0 .. NS-2 in flight (pipelined: also the scores of step 0)
-  issue_step(0, IC<0>{});
-  issue_step(1, IC<1 % NS>{});
-  if constexpr (NS > 2) issue_step(2, IC<2 % NS>{});
-  f32x16 sA[NKB], sB[NKB];
-  if constexpr (PIPE) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * NI));  // K of step 0 has landed
+  // Row maximum of a step's scores (both halves of the wave), in log2 units.
+  auto row_max = [&](const f32x16 (&s)[NKB]) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+    return xhalf_max(mx) * c;
+  };
+  // Raise the running maximum only when the step's maximum exceeds it by
+  // more than the slack; the accumulator and row sum are rescaled then.
+  auto rescale = [&](float mx) {
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+    }
+  };
+  // P = exp2(S c - m), packed to bf16; row sums over the rounded weights.
+  auto exp_pack = [&](const f32x16 (&s)[NKB], bf16x8 (&pk)[NKB][2]) {
+    const float mneg = -m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8 v8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][half * 8 + e], c, mneg)));
+        pk[kb][half] = v8;
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 0, 1), kOnes2, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 2, 3), kOnes2, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 4, 5), kOnes2, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 6, 7), kOnes2, lsum, false);
+      }
+    }
+    l_run += lsum;
+  };
+
+  // ---- plain schedule: per step, S = K Q^T, softmax, O += P V, with the
+  // K and V of the next NS-1 steps landing meanwhile.  Every step issues
+  // exactly one batch (past the end of the key list a harmless re-fetch
+  // of the last key into the free stage), so the wait count is the same
+  // on every step.
+  auto body = [&](int step, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    issue(step + NS - 1, IC<(st + NS - 1) % NS>{}, IC<1>{});
+    issue(step + NS - 1, IC<(st + NS - 1) % NS>{}, IC<0>{});
+    f32x16 s[NKB];
+    qk(stage_c, s);
+    const int j0 = step * KT;
+    if (j0 + KT > n_keys) mask_tail<NKB>(s, n_keys - j0, hh);
+    rescale(row_max(s));
+    bf16x8 pk[NKB][2];
+    exp_pack(s, pk);
+    pv(stage_c, pk);
+    // the next step reads K and V of step+1: batches step+2 .. step+NS-1
+    // may still be in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
     lds_barrier();
-    qk(IC<0>{}, sA);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));  // V of step 0, K of step 1
-    lds_barrier();
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
-    lds_barrier();
+  };
+  // prologue: steps 0 .. NS-2 in flight
+  issue(0, IC<0>{}, IC<1>{});
+  issue(0, IC<0>{}, IC<0>{});
+  if constexpr (NS > 2) {
+    issue(1, IC<1>{}, IC<1>{});
+    issue(1, IC<1>{}, IC<0>{});
+    issue(2, IC<2 % NS>{}, IC<1>{});
+    issue(2, IC<2 % NS>{}, IC<0>{});
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
+  lds_barrier();
   for (int step = 0;;) {
-    body(step, IC<0>{}, sA, sB);
+    body(step, IC<0>{});
     if (++step >= nsteps) break;
-    body(step, IC<1 % NS>{}, sB, sA);
+    body(step, IC<1 % NS>{});
     if (++step >= nsteps) break;
     if constexpr (NS > 2) {
-      body(step, IC<2 % NS>{}, sA, sB);
+      body(step, IC<2 % NS>{});
       if (++step >= nsteps) break;
-      body(step, IC<3 % NS>{}, sB, sA);
+      body(step, IC<3 % NS>{});
       if (++step >= nsteps) break;
     }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA outlives the workgroup
 
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
   __bf16* og = static_cast<__bf16*>(p.out) + bh_off;
@@ -394,24 +385,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// The bf16 kernel: 8 waves x 32 query rows per workgroup, 128 keys per step,
-// 2-stage LDS ring (K and V of step j+1 land while step j computes).  The
-// template also builds 64-key steps over a 4-stage ring with the scores of
-// step j+1 computed under step j's softmax; on the 768p workload that shape
-// measured 3% slower.
+// The bf16 kernel's shape: waves per workgroup (32 query rows each), keys
+// per step and LDS ring stages.
+#ifndef VDN_BF16_NW
+#define VDN_BF16_NW 8
+#endif
 #ifndef VDN_BF16_KT
 #define VDN_BF16_KT 128
 #endif
-#ifndef VDN_BF16_STAGES
-#define VDN_BF16_STAGES 2
+#ifndef VDN_BF16_NS
+#define VDN_BF16_NS 2
 #endif
-#ifndef VDN_BF16_PIPE
-#define VDN_BF16_PIPE 0
+#ifndef VDN_BF16_KPF
+#define VDN_BF16_KPF 4
 #endif
-constexpr int kWaves = 8;
-constexpr int kStages = VDN_BF16_STAGES;
+constexpr int kWaves = VDN_BF16_NW;
 constexpr int kKeysPerStep = VDN_BF16_KT;
-constexpr bool kPipe = VDN_BF16_PIPE != 0;
+constexpr int kStages = VDN_BF16_NS;
+constexpr int kReadAhead = VDN_BF16_KPF;  // K fragments in flight ahead of the QK MFMAs
 
 int kernel_tile_m(int head_dim, int dtype) {
   (void)head_dim;
@@ -426,9 +417,9 @@ int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
   if (dtype == 1) return launch_fwd_fp8(p, head_dim, stream);
   if (dtype != 0) return int(hipErrorInvalidValue);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kPipe>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead>), grid, block, 0, st, p);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kPipe>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
