@@ -43,7 +43,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // log2 of the factor applied to the weights before rounding them to e4m3.
 [[maybe_unused]] constexpr float kFp8PShift = 8.0f;
 
-template <int D, int NW, int NS, int KT, bool PIPE>
+template <int D, int NW, int NS, int KT, int KPF>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int QW = 32;          // query rows per wave
@@ -59,7 +59,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
   constexpr int NPV = KT / 64;    // 64-key PV MFMAs per d block per step
   static_assert(D == 128 && NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
   static_assert(NS == 2 || NS == 4, "the main loop is unrolled for a 2- or 4-stage ring");
-  static_assert(!PIPE || NS == 4, "pipelined scores need K two steps ahead");
   // Row swizzles (16-byte chunk c of key row r stored at c ^ swz(r)):
   //   K: (r >> 1) % 8 -- 16 consecutive rows (two per 256 bytes of banks) of
   //      a 16-byte fragment read land on distinct banks;
@@ -68,6 +67,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
   auto kswz = [](int r) { return (r >> 1) & (CH - 1); };
   auto vswz = [](int r) { return 2 * (((r >> 1) & 1) | ((r >> 2) & 2)); };
 
+  // K and V rings, one LDS array per stage (measured 1-2% faster than one
+  // array holding all stages).  The DMA is inline asm that the compiler does
+  // not track: stage reuse is ordered by explicit vmcnt waits and barriers.
   constexpr int T2 = NS > 2 ? TILE : 16;  // stages 2 and 3 exist only in the 4-stage ring
   __shared__ __attribute__((aligned(1024))) char Ks0[TILE];
   __shared__ __attribute__((aligned(1024))) char Ks1[TILE];
@@ -216,44 +218,60 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
   const int nsteps = (n_keys + KT - 1) / KT;
   const i32x8 ones8 = {kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones, kFp8Ones};
 
+  // S^T = K Q^T; the K fragments (two 16-byte reads each) run KPF MFMAs
+  // ahead of their consumers, pinned there against the scheduler.
   auto qk = [&](auto stage_c, f32x16 (&s)[NKB]) {
     const char* ks = kstage(stage_c);
+    constexpr int NF = NQK * NKB;
+    constexpr int PF = KPF < NF ? KPF : NF;
+    auto frag = [&](int f) {
+      const int m = f / NKB, kb = f % NKB;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(ks + kb * 32 * RB + k_roff[m][0]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(ks + kb * 32 * RB + k_roff[m][1]);
+      return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    i32x8 fr[PF];
+#pragma unroll
+    for (int f = 0; f < PF; ++f) fr[f] = frag(f);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-    for (int m = 0; m < NQK; ++m) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(ks + kb * 32 * RB + k_roff[m][0]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(ks + kb * 32 * RB + k_roff[m][1]);
-        const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q8[m], s[kb], 0, 0, 0, 0, 0, 0);
-      }
+    for (int f = 0; f < NF; ++f) {
+      s[f % NKB] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fr[f % PF], q8[f / NKB], s[f % NKB], 0, 0, 0, 0, 0, 0);
+      if (f + PF < NF) fr[f % PF] = frag(f + PF);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // the next step reads K and V of step+1: batches step+2 .. step+NS-1 may
+  // still be in flight
   auto sync_step = [&]() {
-    if constexpr (PIPE) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));
-    } else {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
-    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
     lds_barrier();
   };
+  // a wave whose rows all lie past the end of the query block only helps
+  // with the DMA and the barriers
+  const bool active = __builtin_amdgcn_readfirstlane(wave) * QW < rows;
 
-  auto body = [&](int step, auto stage_c, f32x16 (&s_cur)[NKB], f32x16 (&s_next)[NKB]) {
-    constexpr int st = decltype(stage_c)::value;
-    issue_step(step + NS - 1, IC<(st + NS - 1) % NS>{});
-    if constexpr (!PIPE) qk(stage_c, s_cur);
-
+  auto compute = [&](int step, auto stage_c) {
+    f32x16 s_cur[NKB];
+    qk(stage_c, s_cur);
     const int j0 = step * KT;
     if (j0 + KT > n_keys) mask_tail<NKB>(s_cur, n_keys - j0, hh);
     {
-      float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
+      // one running maximum per key block folding two scores per three-input
+      // max (the compiler's own form needs 3 ops per 4 scores)
+      float mb[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb) {
+        mb[kb] = fmaxf(s_cur[kb][0], s_cur[kb][1]);
 #pragma unroll
-        for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[kb][r], s_cur[kb][r + 1]));
+        for (int r = 2; r < 16; r += 2)
+          asm("v_max3_f32 %0, %0, %1, %2" : "+v"(mb[kb]) : "v"(s_cur[kb][r]), "v"(s_cur[kb][r + 1]));
+      }
+      float mx = mb[0];
+#pragma unroll
+      for (int kb = 1; kb < NKB; ++kb) mx = fmaxf(mx, mb[kb]);
       mx = xhalf_max(mx) * c;
       if (__any(mx > m_run)) {
         const float m_new = fmaxf(m_run, mx);
@@ -267,8 +285,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
           for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
       }
     }
-
-    if constexpr (PIPE) qk(IC<(st + 1) % NS>{}, s_next);
 
     // P = 2^8 exp2(S c - m) <= 2^8, rounded to e4m3: byte 16 (kb % 2) + r of
     // the lane's operand for PV MFMA kb / 2
@@ -306,35 +322,35 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
         acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, p8[t], acc[db], 0, 0, 0, 0, 0, 0);
       }
     }
+  };
+  auto body = [&](int step, auto stage_c) {
+    constexpr int st = decltype(stage_c)::value;
+    issue_step(step + NS - 1, IC<(st + NS - 1) % NS>{});
+    if (active) compute(step, stage_c);
     sync_step();
   };
 
+  // prologue: steps 0 .. NS-2 in flight
   issue_step(0, IC<0>{});
-  issue_step(1, IC<1 % NS>{});
-  if constexpr (NS > 2) issue_step(2, IC<2 % NS>{});
-  f32x16 sA[NKB], sB[NKB];
-  if constexpr (PIPE) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * NI));  // K of step 0 has landed
-    lds_barrier();
-    qk(IC<0>{}, sA);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * NI));  // V of step 0, K of step 1
-    lds_barrier();
-  } else {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
-    lds_barrier();
+  if constexpr (NS > 2) {
+    issue_step(1, IC<1>{});
+    issue_step(2, IC<2 % NS>{});
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
+  lds_barrier();
   for (int step = 0;;) {
-    body(step, IC<0>{}, sA, sB);
+    body(step, IC<0>{});
     if (++step >= nsteps) break;
-    body(step, IC<1 % NS>{}, sB, sA);
+    body(step, IC<1 % NS>{});
     if (++step >= nsteps) break;
     if constexpr (NS > 2) {
-      body(step, IC<2 % NS>{}, sA, sB);
+      body(step, IC<2 % NS>{});
       if (++step >= nsteps) break;
-      body(step, IC<3 % NS>{}, sB, sA);
+      body(step, IC<3 % NS>{});
       if (++step >= nsteps) break;
     }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA outlives the workgroup
 
   // ---- epilogue: O = acc * s_v / l (* gate), bf16
   __bf16* og = static_cast<__bf16*>(p.out) + (int64_t(b) * p.S * p.H + int64_t(h)) * D;
@@ -365,28 +381,28 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// 128 keys per step over a 2-stage ring: on the 768p fp8 workload this
-// measured 10% faster than 64-key steps with the next step's scores
-// pipelined under the softmax (both shapes build from the template).
+// 128 keys per step over a 2-stage ring (64-key steps with the next
+// step's scores pipelined under the softmax measured 10% slower on the 768p
+// fp8 workload); K fragments 4 MFMAs ahead.
 #ifndef VDN_FP8_KT
 #define VDN_FP8_KT 128
 #endif
 #ifndef VDN_FP8_STAGES
 #define VDN_FP8_STAGES 2
 #endif
-#ifndef VDN_FP8_PIPE
-#define VDN_FP8_PIPE 0
+#ifndef VDN_FP8_KPF
+#define VDN_FP8_KPF 4
 #endif
 
 int launch_fwd_fp8(const FwdParams& p, int head_dim, void* stream) {
   constexpr int kWaves = 8;
   constexpr int kStages = VDN_FP8_STAGES;
   constexpr int kKeysPerStep = VDN_FP8_KT;
-  constexpr bool kPipe = VDN_FP8_PIPE != 0;
+  constexpr int kReadAhead = VDN_FP8_KPF;
   const dim3 grid(unsigned(p.per_xcd) * 8u);
   const dim3 block(64 * kWaves);
   if (head_dim != 128) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL((fwd_fp8_kernel<128, kWaves, kStages, kKeysPerStep, kPipe>), grid, block, 0, static_cast<hipStream_t>(stream), p);
+  hipLaunchKernelGGL((fwd_fp8_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead>), grid, block, 0, static_cast<hipStream_t>(stream), p);
   return int(hipGetLastError());
 }
 

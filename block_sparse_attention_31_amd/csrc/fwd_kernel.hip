@@ -50,7 +50,7 @@ namespace vdn {
 // 16 lanes, lane i receives element (i % 4) of the 8-byte blocks addressed by
 // lanes 4e + i/4 (e = 0..3), so if those lanes point at keys k+e, columns
 // d0 + 4(i/4).., lane i holds V[k..k+3][d0 + i]: the MFMA A-operand layout.
-template <int D, int NW, int NS, int KT, int KPF>
+template <int D, int NW, int NS, int KT, int KPF, int VPF>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int QW = 32;          // query rows per wave
@@ -69,9 +69,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // the 32 lanes of a transposing read (4 keys x 32 columns) cover all banks.
   auto vswz = [](int r) { return (4 * (r & 3)) % CH; };
 
-  // One array per stage and tensor, so that alias analysis can tell a DMA
-  // into one stage from reads of another and the compiler's own waits on
-  // the DMA stay precise.
+  // K and V rings, one LDS array per stage (measured 1-2% faster than one
+  // array holding all stages).  The DMA is inline asm that the compiler does
+  // not track: stage reuse is ordered by explicit vmcnt waits and barriers.
   constexpr int T2 = NS > 2 ? TILE : 16;  // stages 2 and 3 exist only in the 4-stage ring
   __shared__ __attribute__((aligned(1024))) char Ks0[TILE];
   __shared__ __attribute__((aligned(1024))) char Ks1[TILE];
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // clamped to its last key and masked out of the softmax).
   // (the tensor is a compile-time tag: choosing between the two offset arrays
   // at run time would force them out of registers)
-  auto issue = [&](int step, auto stage_c, auto is_k_c) {
+  auto issue = [&](int step, char* lbase, auto is_k_c) {
     constexpr bool is_k = decltype(is_k_c)::value != 0;
     uint32_t goff[NI];
 #pragma unroll
@@ -170,7 +170,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       }
     }
     const char* gbase = is_k ? kg : vg;
-    char* lbase = is_k ? kstage(stage_c) : vstage(stage_c);
     const int j0 = step * KT;
     // interval holding j0, its end and offset (scalar selects)
     const int iv_end = interval_end(kl, j0);
@@ -211,6 +210,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   }
   auto v_roff = [&](int db) { return v_roff0 ^ uint32_t(64 * db); };
 
+  // a wave whose rows all lie past the end of the query block (the last
+  // tile of a block) only helps with the DMA and the barriers
+  const bool active = __builtin_amdgcn_readfirstlane(wave) * 32 < rows;
   const float c = p.score_scale_log2;
   const int nsteps = (n_keys + KT - 1) / KT;
   const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
@@ -218,8 +220,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // S^T = K Q^T for the KT keys in K stage `stage_c`.  The K fragments run
   // KPF reads ahead of the MFMAs that consume them (a read issued just
   // before its MFMA leaves the LDS latency on the critical path).
-  auto qk = [&](auto stage_c, f32x16 (&s)[NKB]) {
-    const char* ks = kstage(stage_c);
+  auto qk = [&](const char* ks, f32x16 (&s)[NKB]) {
     constexpr int NF = NDS * NKB;  // fragments (= MFMAs) per step
     constexpr int PF = KPF < NF ? KPF : NF;
     auto frag = [&](int f) {
@@ -244,33 +245,43 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 
   // O^T += V^T P^T for the KT keys in V stage `stage_c` (V^T fragments by
   // transposing LDS reads).
-  auto pv = [&](auto stage_c, const bf16x8 (&pk)[NKB][2]) {
-    const char* vs = vstage(stage_c);
+  auto pv = [&](const char* vs, const bf16x8 (&pk)[NKB][2]) {
+    constexpr int NF = NKB * 2 * NDB;  // fragments (= MFMAs) per step: (kb, half, db)
+    constexpr int PF = VPF < NF ? VPF : NF;
+    auto frag = [&](int f) {
+      const int db = f % NDB, kh = f / NDB;  // kh = 2 kb + half
+      const char* base = vs + kh * 16 * RB + v_roff(db);
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + 8 * RB));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 fr[PF];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int f = 0; f < PF; ++f) fr[f] = frag(f);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const char* base = vs + (kb * 32 + half * 16) * RB + v_roff(db);
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(base));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(base + 8 * RB));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb][half], acc[db], 0, 0, 0);
-        }
-      }
+    for (int f = 0; f < NF; ++f) {
+      const int db = f % NDB, kh = f / NDB;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % PF], pk[kh / 2][kh % 2], acc[db], 0, 0, 0);
+      if (f + PF < NF) fr[f % PF] = frag(f + PF);
     }
   };
 
   // Row maximum of a step's scores (both halves of the wave), in log2 units.
   auto row_max = [&](const f32x16 (&s)[NKB]) {
-    float mx = fmaxf(s[0][0], s[0][1]);
+    // one running maximum per key block, each step folding two scores with
+    // a three-input max (the compiler's own form takes a two-input max per
+    // pair and a three-input max per two pairs: 3 ops per 4 scores, not 2)
+    float mb[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      mb[kb] = fmaxf(s[kb][0], s[kb][1]);
 #pragma unroll
-      for (int r = (kb == 0 ? 2 : 0); r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+      for (int r = 2; r < 16; r += 2)
+        asm("v_max3_f32 %0, %0, %1, %2" : "+v"(mb[kb]) : "v"(s[kb][r]), "v"(s[kb][r + 1]));
+    }
+    float mx = mb[0];
+#pragma unroll
+    for (int kb = 1; kb < NKB; ++kb) mx = fmaxf(mx, mb[kb]);
     return xhalf_max(mx) * c;
   };
   // Raise the running maximum only when the step's maximum exceeds it by
@@ -309,36 +320,38 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     l_run += lsum;
   };
 
-  // ---- plain schedule: per step, S = K Q^T, softmax, O += P V, with the
+  // ---- main loop: per step, S = K Q^T, softmax, O += P V, with the
   // K and V of the next NS-1 steps landing meanwhile.  Every step issues
   // exactly one batch (past the end of the key list a harmless re-fetch
   // of the last key into the free stage), so the wait count is the same
   // on every step.
   auto body = [&](int step, auto stage_c) {
     constexpr int st = decltype(stage_c)::value;
-    issue(step + NS - 1, IC<(st + NS - 1) % NS>{}, IC<1>{});
-    issue(step + NS - 1, IC<(st + NS - 1) % NS>{}, IC<0>{});
-    f32x16 s[NKB];
-    qk(stage_c, s);
-    const int j0 = step * KT;
-    if (j0 + KT > n_keys) mask_tail<NKB>(s, n_keys - j0, hh);
-    rescale(row_max(s));
-    bf16x8 pk[NKB][2];
-    exp_pack(s, pk);
-    pv(stage_c, pk);
+    issue(step + NS - 1, kstage(IC<(st + NS - 1) % NS>{}), IC<1>{});
+    issue(step + NS - 1, vstage(IC<(st + NS - 1) % NS>{}), IC<0>{});
+    if (active) {
+      f32x16 s[NKB];
+      qk(kstage(stage_c), s);
+      const int j0 = step * KT;
+      if (j0 + KT > n_keys) mask_tail<NKB>(s, n_keys - j0, hh);
+      rescale(row_max(s));
+      bf16x8 pk[NKB][2];
+      exp_pack(s, pk);
+      pv(vstage(stage_c), pk);
+    }
     // the next step reads K and V of step+1: batches step+2 .. step+NS-1
     // may still be in flight
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
     lds_barrier();
   };
   // prologue: steps 0 .. NS-2 in flight
-  issue(0, IC<0>{}, IC<1>{});
-  issue(0, IC<0>{}, IC<0>{});
+  issue(0, kstage(IC<0>{}), IC<1>{});
+  issue(0, vstage(IC<0>{}), IC<0>{});
   if constexpr (NS > 2) {
-    issue(1, IC<1>{}, IC<1>{});
-    issue(1, IC<1>{}, IC<0>{});
-    issue(2, IC<2 % NS>{}, IC<1>{});
-    issue(2, IC<2 % NS>{}, IC<0>{});
+    issue(1, kstage(IC<1>{}), IC<1>{});
+    issue(1, vstage(IC<1>{}), IC<0>{});
+    issue(2, kstage(IC<2 % NS>{}), IC<1>{});
+    issue(2, vstage(IC<2 % NS>{}), IC<0>{});
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
   lds_barrier();
@@ -403,6 +416,10 @@ constexpr int kWaves = VDN_BF16_NW;
 constexpr int kKeysPerStep = VDN_BF16_KT;
 constexpr int kStages = VDN_BF16_NS;
 constexpr int kReadAhead = VDN_BF16_KPF;  // K fragments in flight ahead of the QK MFMAs
+#ifndef VDN_BF16_VPF
+#define VDN_BF16_VPF 2
+#endif
+constexpr int kReadAheadV = VDN_BF16_VPF;  // V^T fragments in flight ahead of the PV MFMAs
 
 int kernel_tile_m(int head_dim, int dtype) {
   (void)head_dim;
@@ -417,9 +434,9 @@ int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
   if (dtype == 1) return launch_fwd_fp8(p, head_dim, stream);
   if (dtype != 0) return int(hipErrorInvalidValue);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV>), grid, block, 0, st, p);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
