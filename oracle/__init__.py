@@ -17,6 +17,12 @@ values from the pages' description):
                                             closed forms, needle probes
 * ``attend_dense_masked``                -- torch SDPA with a boolean mask
 * ``dequantize_fp8``                     -- exact products checked by hand
+* ``key_blocks``                         -- column scan of the explicit mask
+* ``attend_backward``                    -- torch autograd (float64) through
+                                            dense masked attention, central
+                                            finite differences, closed forms
+                                            (constant values, zero queries,
+                                            keys' gradients summing to zero)
 
 No function here is "parity unpinned".
 """
@@ -30,7 +36,9 @@ from .local_attn import (  # noqa: F401
     count_pairs,
     count_pairs_bruteforce,
     attend,
+    attend_backward,
     attend_dense_masked,
+    key_blocks,
     dequantize_fp8,
     sigmoid,
 )

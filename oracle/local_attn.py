@@ -255,3 +255,105 @@ def attend_dense_masked(q, k, v, gate, mask: np.ndarray, scale: float | None = N
             out[b, :, h, :] = o
             lse[b, h, :] = ls
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Backward pass (gradients of the forward above)
+# --------------------------------------------------------------------------
+#
+# The pages train low-rank adapters on the attention projections through this
+# branch (superapi "Technical Principles", training stages), so gradients
+# flow back through it.  They state no formula: the gradient of the forward
+# defined above is its derivative, written out here by the chain rule.  With
+# p_ij = softmax_j(s_i) over the key set, a_i = sum_j p_ij v_j (before the
+# gate), sg_i = sigmoid(g_i) and out_i = sg_i a_i, for an upstream gradient
+# dout:
+#   da_i    = sg_i dout_i
+#   dg_i    = (dout_i . a_i) sg_i (1 - sg_i)
+#   dp_ij   = da_i . v_j
+#   ds_ij   = p_ij (dp_ij - sum_k p_ik dp_ik)        (softmax derivative)
+#   dq_i    = scale sum_j ds_ij k_j
+#   dk_j    = scale sum_i ds_ij q_i                  (over queries that see j)
+#   dv_j    = sum_i p_ij da_i
+
+
+def key_blocks(F: int, T: int, N: int, Bf: int) -> list[tuple[list[tuple[int, int]], list[tuple[int, int]]]]:
+    """The key side of the key structure: groups of keys that are seen by the
+    same query rows, as (key intervals, query intervals), both canonical.
+
+    Read off the rule of :func:`allowed_mask` column-wise: a video key whose
+    frame is not an anchor, in frame block b, is seen by the video queries of
+    blocks b-1 .. b+1 (the same frame range as :func:`window_frames` of b) and
+    by every text query; anchor-frame keys and text keys are seen by every
+    query.  One group per frame block (its non-anchor frames; omitted when
+    empty), then the group of anchor and text keys (omitted when empty)."""
+    V = F * T
+    S = V + N
+    out = []
+    for beta in range(num_frame_blocks(F, Bf)):
+        f0, f1 = beta * Bf, min(F, (beta + 1) * Bf)
+        frames = [f for f in range(f0, f1) if f != 0 and f != F - 1]
+        if not frames or T == 0:
+            continue
+        keys = _merge([(f * T, (f + 1) * T) for f in frames])
+        lo, hi = window_frames(beta, F, Bf)
+        out.append((keys, _merge([(lo * T, hi * T), (V, S)])))
+    glob = _merge([(0, T), ((F - 1) * T, F * T), (V, S)])
+    if glob:
+        out.append((glob, [(0, S)]))
+    return out
+
+
+def _gate_backward(do, a, sg):
+    """Through out = sg * a: (da, dg) = (sg do, (do . a) sg (1 - sg))."""
+    return do * sg[:, None], np.sum(do * a, axis=1) * sg * (1.0 - sg)
+
+
+def _softmax_backward(p, dp):
+    """Through a row softmax p: ds = p (dp - sum_k p_k dp_k)."""
+    return p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+
+
+def attend_backward(q, k, v, gate, dout, F: int, T: int, N: int, Bf: int,
+                    scale: float | None = None, row_chunk: int = 2048):
+    """Gradients of :func:`attend` in fp64: returns (dq, dk, dv, dgate) with
+    the shapes of q, k, v and gate (dgate is None without a gate).
+
+    Query block by query block: recompute the softmax over the block's key set
+    as the forward does, then apply the chain rule written out in the comment
+    above; the key gradients are scattered back to the gathered keys."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, H, D = q.shape
+    assert S == F * T + N, (S, F, T, N)
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dgate = None if gate is None else np.zeros((B, S, H))
+    for (r0, r1), ivs in zip(query_blocks(F, T, N, Bf), key_intervals(F, T, N, Bf)):
+        keys = np.concatenate([np.arange(a, b) for a, b in ivs])
+        for b in range(B):
+            for h in range(H):
+                kb = k[b, keys, h, :]
+                vb = v[b, keys, h, :]
+                for c0 in range(r0, r1, row_chunk):
+                    qi = np.arange(c0, min(r1, c0 + row_chunk))
+                    s = (q[b, qi, h, :] @ kb.T) * scale
+                    p, _ = _softmax_rows(s)
+                    a = p @ vb
+                    do = dout[b, qi, h, :]
+                    if gate is not None:
+                        da, dg = _gate_backward(do, a, sigmoid(np.asarray(gate)[b, qi, h]))
+                        dgate[b, qi, h] = dg
+                    else:
+                        da = do
+                    dp = da @ vb.T
+                    ds = _softmax_backward(p, dp)
+                    dq[b, qi, h, :] = scale * (ds @ kb)
+                    np.add.at(dk[b, :, h, :], keys, scale * (ds.T @ q[b, qi, h, :]))
+                    np.add.at(dv[b, :, h, :], keys, p.T @ da)
+    return dq, dk, dv, dgate
