@@ -34,10 +34,12 @@ _pi32 = ctypes.POINTER(ctypes.c_int32)
 _pint = ctypes.POINTER(ctypes.c_int)
 SIGNATURES = {
     "vdn_local_attn_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _f, _p, _p]),
+    "vdn_local_attn_bwd": (_i, [_p] * 11 + [_i] * 7 + [_f, _p, _p]),
     "vdn_local_attn_num_query_blocks": (_i, [_i, _i, _i, _i]),
     "vdn_local_attn_key_intervals": (_i, [_i, _i, _i, _i, _pi64, _pi64, _i, _pint]),
     "vdn_local_attn_count_pairs": (_i, [_i, _i, _i, _i, _pi64, _pi64]),
     "vdn_local_attn_tile_schedule": (_i, [_i, _i, _i, _i, _i, _pi32, _i, _pint]),
+    "vdn_local_attn_key_blocks": (_i, [_i, _i, _i, _i, _pi64, _pi64, _i, _pint]),
     "vdn_local_attn_kernel_tile_m": (_i, [_i, _i]),
     "vdn_last_error": (ctypes.c_char_p, []),
 }
@@ -126,6 +128,26 @@ def vdn_local_attn_tile_schedule(F: int, tokens_per_frame: int, n_text: int, blo
     return [tuple(buf[4 * i:4 * i + 4]) for i in range(n.value)]
 
 
+def vdn_local_attn_key_blocks(F: int, tokens_per_frame: int, n_text: int, block_frames: int):
+    """Returns [(key intervals [(lo, hi)], query intervals [(lo, hi)])]."""
+    n = ctypes.c_int(0)
+    rc = lib().vdn_local_attn_key_blocks(F, tokens_per_frame, n_text, block_frames, None, None, 0,
+                                         ctypes.byref(n))
+    if rc not in (0, -6):
+        _check(rc)
+    cap = max(n.value, 1)
+    kiv = (ctypes.c_int64 * (2 * VDN_MAX_KEY_INTERVALS * cap))()
+    qiv = (ctypes.c_int64 * (2 * VDN_MAX_KEY_INTERVALS * cap))()
+    _check(lib().vdn_local_attn_key_blocks(F, tokens_per_frame, n_text, block_frames, kiv, qiv, cap,
+                                           ctypes.byref(n)))
+
+    def unpack(buf, i):
+        base = 2 * VDN_MAX_KEY_INTERVALS * i
+        return [(buf[base + 2 * j], buf[base + 2 * j + 1]) for j in range(VDN_MAX_KEY_INTERVALS)
+                if buf[base + 2 * j] >= 0]
+    return [(unpack(kiv, i), unpack(qiv, i)) for i in range(n.value)]
+
+
 def vdn_local_attn_kernel_tile_m(head_dim: int, dtype: int) -> int:
     return _check(lib().vdn_local_attn_kernel_tile_m(head_dim, dtype))
 
@@ -198,3 +220,54 @@ def local_attn_fwd(q, k, v, gate=None, *, F: int, tokens_per_frame: int, n_text:
     vdn_local_attn_fwd(q, k, v, gate, out, F, tokens_per_frame, n_text, block_frames,
                        qkv_scales=qkv_scales, softmax_scale=softmax_scale, lse=lse)
     return (out, lse) if return_lse else out
+
+
+# ----------------------------------------------------------------- backward
+
+
+def vdn_local_attn_bwd(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, F: int,
+                       tokens_per_frame: int, n_text: int, block_frames: int = 5,
+                       softmax_scale: float = 0.0, workspace=None, stream=None) -> None:
+    """Enqueue the backward pass on `stream` (default: torch's current stream).
+
+    q, k, v, out, dout, dq, dk, dv: [B, S, H, D] bf16 CUDA tensors; gate and
+    dgate [B, S, H] fp32 (both or neither); lse [B, H, S] fp32 (the forward's);
+    workspace: fp32 CUDA tensor of at least 2*B*H*S elements."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    B, S, H, D = q.shape
+    if workspace is None or workspace.numel() < 2 * B * H * S:
+        raise ValueError(f"workspace must hold at least {2 * B * H * S} fp32 values")
+    for name, t, shape in (("gate", gate, (B, S, H)), ("dgate", dgate, (B, S, H)),
+                           ("lse", lse, (B, H, S)), ("workspace", workspace, None)):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a contiguous fp32 GPU tensor")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().vdn_local_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), F, tokens_per_frame, n_text, block_frames,
+        H, D, B, float(softmax_scale), _ptr(workspace), ctypes.c_void_p(stream))
+    _check(rc)
+
+
+def local_attn_bwd(q, k, v, gate, out, dout, lse, *, F: int, tokens_per_frame: int, n_text: int,
+                   block_frames: int = 5, softmax_scale: float = 0.0):
+    """Allocating convenience wrapper: returns (dq, dk, dv, dgate or None)."""
+    import torch
+    B, S, H, D = q.shape
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    dgate = None if gate is None else torch.empty((B, S, H), dtype=torch.float32, device=q.device)
+    ws = torch.empty(2 * B * H * S, dtype=torch.float32, device=q.device)
+    vdn_local_attn_bwd(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, F, tokens_per_frame, n_text,
+                       block_frames, softmax_scale=softmax_scale, workspace=ws)
+    return dq, dk, dv, dgate

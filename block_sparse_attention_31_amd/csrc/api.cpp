@@ -6,6 +6,8 @@
 #include <cstdint>
 #include <cstring>
 #include <string>
+#include <vector>
+#include <algorithm>
 
 #include "../../include/vdn_local_attn.h"
 #include "fwd_params.hpp"
@@ -110,6 +112,36 @@ int vdn_local_attn_tile_schedule(int F, int tokens_per_frame, int n_text, int bl
     out[4 * i + 1] = tiles[i].row0;
     out[4 * i + 2] = tiles[i].rows;
     out[4 * i + 3] = tiles[i].keys;
+  }
+  return ok();
+}
+
+int vdn_local_attn_key_blocks(int F, int tokens_per_frame, int n_text, int block_frames,
+                              int64_t* key_intervals, int64_t* query_intervals, int capacity,
+                              int* n_kblocks) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  if (n_kblocks == nullptr) return fail(VDN_ERR_INVALID_ARG, "n_kblocks is NULL");
+  const auto blocks = vdn::build_key_blocks(g);
+  *n_kblocks = int(blocks.size());
+  if (capacity < int(blocks.size()))
+    return fail(VDN_ERR_CAPACITY, "capacity " + std::to_string(capacity) + " < " +
+                                      std::to_string(blocks.size()) + " key blocks");
+  for (size_t i = 0; i < blocks.size(); ++i) {
+    const vdn::KeyBlock& kb = blocks[i];
+    for (int side = 0; side < 2; ++side) {
+      int64_t* base = side == 0 ? key_intervals : query_intervals;
+      if (base == nullptr) continue;
+      int64_t* dst = base + i * VDN_MAX_KEY_INTERVALS * 2;
+      const int n = side == 0 ? kb.n_kiv : kb.n_qiv;
+      const vdn::Interval* iv = side == 0 ? kb.kiv : kb.qiv;
+      for (int j = 0; j < VDN_MAX_KEY_INTERVALS; ++j) {
+        dst[2 * j] = j < n ? iv[j].lo : -1;
+        dst[2 * j + 1] = j < n ? iv[j].hi : -1;
+      }
+    }
   }
   return ok();
 }
@@ -219,6 +251,152 @@ int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float*
   p.per_xcd = (p.total_tiles + 7) / 8;
 
   const int rc = vdn::launch_fwd(p, head_dim, dtype, hip_stream);
+  if (rc != 0)
+    return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
+  return ok();
+}
+
+int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float* gate,
+                       const void* out, const void* dout, const float* lse, void* dq, void* dk,
+                       void* dv, float* dgate, int F, int tokens_per_frame, int n_text,
+                       int block_frames, int heads, int head_dim, int batch, float softmax_scale,
+                       float* workspace, void* hip_stream) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  if (heads <= 0 || batch <= 0)
+    return fail(VDN_ERR_INVALID_ARG, "heads and batch must be >= 1");
+  const void* need[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
+  for (const void* x : need)
+    if (x == nullptr)
+      return fail(VDN_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk, dv and workspace must be non-NULL");
+  if ((gate == nullptr) != (dgate == nullptr))
+    return fail(VDN_ERR_INVALID_ARG, "dgate must be given exactly when gate is");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got " + std::to_string(head_dim) + ")");
+  if (!std::isfinite(softmax_scale))
+    return fail(VDN_ERR_INVALID_ARG, "softmax_scale is not finite");
+  const void* a16[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* x : a16)
+    if (!aligned(x, 16)) return fail(VDN_ERR_ALIGNMENT, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(gate, 4) || !aligned(lse, 4) || !aligned(dgate, 4) || !aligned(workspace, 4))
+    return fail(VDN_ERR_ALIGNMENT, "gate, lse, dgate and workspace must be 4-byte aligned");
+  if (g.S > INT32_MAX / 2)
+    return fail(VDN_ERR_OVERFLOW, "sequence length " + std::to_string(g.S) + " too large");
+  const int64_t elems = int64_t(batch) * g.S * int64_t(heads) * int64_t(head_dim);
+  if (elems / batch / heads / head_dim != g.S || elems > (int64_t(1) << 46))
+    return fail(VDN_ERR_OVERFLOW, "tensor element count overflows");
+  if (int64_t(batch) * heads > INT32_MAX / 4096)
+    return fail(VDN_ERR_OVERFLOW, "batch * heads too large");
+
+  const size_t t_bytes = size_t(elems) * 2u;
+  const size_t row_bytes = size_t(batch) * size_t(g.S) * size_t(heads) * 4u;
+  const void* ins[] = {q, k, v, out, dout, lse, gate};
+  const size_t in_sz[] = {t_bytes, t_bytes, t_bytes, t_bytes, t_bytes, row_bytes, gate ? row_bytes : 0u};
+  const void* outs[] = {dq, dk, dv, dgate, workspace};
+  const size_t out_sz[] = {t_bytes, t_bytes, t_bytes, dgate ? row_bytes : 0u, 2 * row_bytes};
+  for (int i = 0; i < 5; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j]))
+        return fail(VDN_ERR_INVALID_ARG, "an output or the workspace overlaps an input");
+    for (int j = i + 1; j < 5; ++j)
+      if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j]))
+        return fail(VDN_ERR_INVALID_ARG, "outputs and workspace must not overlap each other");
+  }
+
+  const auto qblocks = vdn::build_query_blocks(g);
+  const auto kblocks = vdn::build_key_blocks(g);
+  if (int(qblocks.size()) > vdn::kMaxQueryBlocks || int(kblocks.size()) > vdn::kMaxQueryBlocks)
+    return fail(VDN_ERR_UNSUPPORTED, "more than " + std::to_string(vdn::kMaxQueryBlocks) + " query blocks");
+
+  vdn::BwdDqParams dq_p;
+  vdn::BwdKvParams kv_p;
+  std::memset(&dq_p, 0, sizeof(dq_p));
+  std::memset(&kv_p, 0, sizeof(kv_p));
+  vdn::BwdArgs& a = dq_p.a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.gate = gate;
+  a.lse = lse;
+  a.delta = workspace;
+  a.sg = workspace + size_t(batch) * size_t(heads) * size_t(g.S);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dgate = dgate;
+  a.B = batch;
+  a.S = int32_t(g.S);
+  a.H = heads;
+  const float sm = softmax_scale > 0.f ? softmax_scale : float(1.0 / std::sqrt(double(head_dim)));
+  a.scale = sm;
+  a.score_scale_log2 = float(double(sm) * 1.4426950408889634);
+  kv_p.a = a;
+
+  // dQ: query tiles, longest key list first
+  const int tile_m = vdn::bwd_dq_tile_m();
+  int prefix = 0, n = 0;
+  for (int bi : vdn::cost_order(qblocks)) {
+    const vdn::QueryBlock& qb = qblocks[size_t(bi)];
+    vdn::QBlockDesc& d = dq_p.blk[n++];
+    d.row_lo = int32_t(qb.row_lo);
+    d.rows = int32_t(qb.row_hi - qb.row_lo);
+    d.n_keys = int32_t(qb.n_keys);
+    d.tile_prefix = prefix;
+    d.n_iv = qb.n_iv;
+    int64_t start = 0;
+    for (int i = 0; i < qb.n_iv; ++i) {
+      d.iv_start[i] = int32_t(start);
+      d.iv_delta[i] = int32_t(qb.iv[i].lo - start);
+      start += qb.iv[i].hi - qb.iv[i].lo;
+    }
+    prefix += (d.rows + tile_m - 1) / tile_m;
+  }
+  dq_p.n_blocks = n;
+  dq_p.tiles_per_bh = prefix;
+  dq_p.total_tiles = prefix * batch * heads;
+  dq_p.per_xcd = (dq_p.total_tiles + 7) / 8;
+
+  // dK/dV: key tiles, most query rows first
+  const int tile_n = vdn::bwd_dkv_tile_n();
+  std::vector<int> korder(kblocks.size());
+  for (size_t i = 0; i < korder.size(); ++i) korder[i] = int(i);
+  std::stable_sort(korder.begin(), korder.end(), [&](int x, int y) {
+    return kblocks[size_t(x)].n_rows > kblocks[size_t(y)].n_rows;
+  });
+  prefix = 0;
+  n = 0;
+  for (int ki : korder) {
+    const vdn::KeyBlock& kb = kblocks[size_t(ki)];
+    vdn::KBlockDesc& d = kv_p.blk[n++];
+    d.n_keys = int32_t(kb.n_keys);
+    d.n_rows = int32_t(kb.n_rows);
+    d.tile_prefix = prefix;
+    int64_t start = 0;
+    d.kiv_start[0] = d.kiv_start[1] = d.n_keys;
+    for (int i = 0; i < kb.n_kiv; ++i) {
+      if (i > 0) d.kiv_start[i - 1] = int32_t(start);
+      d.kiv_delta[i] = int32_t(kb.kiv[i].lo - start);
+      start += kb.kiv[i].hi - kb.kiv[i].lo;
+    }
+    start = 0;
+    d.qiv_start = d.n_rows;
+    for (int i = 0; i < kb.n_qiv; ++i) {
+      if (i > 0) d.qiv_start = int32_t(start);
+      d.qiv_delta[i] = int32_t(kb.qiv[i].lo - start);
+      start += kb.qiv[i].hi - kb.qiv[i].lo;
+    }
+    prefix += (d.n_keys + tile_n - 1) / tile_n;
+  }
+  kv_p.n_blocks = n;
+  kv_p.tiles_per_bh = prefix;
+  kv_p.total_tiles = prefix * batch * heads;
+  kv_p.per_xcd = (kv_p.total_tiles + 7) / 8;
+
+  const int rc = vdn::launch_bwd(dq_p, kv_p, head_dim, hip_stream);
   if (rc != 0)
     return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
   return ok();

@@ -1,0 +1,572 @@
+// Backward pass of the local-window attention for gfx950, bf16 inputs.
+//
+// Gradients of the forward (local Softmax branch of VDN-H3 attention:
+// frame-block window, first/last-frame anchors, global text keys, per-token
+// sigmoid gate; openi.cn "VDN-MiniMax-H3", technical principles;
+// nav.superapi.store "VDN-MiniMax-H3 - OpenVDN's Open-Source Video Generation
+// Acceleration Solution", Technical Principles and training stages, where
+// adapters on the attention projections are trained through this branch).
+// With p_ij = exp(scale q_i.k_j - lse_i) over the key set, sg_i = sigmoid of
+// the gate logit and out_i = sg_i sum_j p_ij v_j:
+//   delta_i = sum_d dout_i out_i        (the gate cancels: dout.a sg = dout.out)
+//   dgate_i = delta_i (1 - sg_i)
+//   dp_ij   = dout_i . v_j
+//   ds_ij   = p_ij (sg_i dp_ij - delta_i)
+//   dq_i    = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+//   dv_j    = sum_i sg_i p_ij dout_i.
+// Three kernels: a per-row pass (delta, sg, dgate), dQ over query tiles with
+// the keys streaming through LDS (the forward's schedule), and dK/dV over key
+// tiles with the query rows streaming through LDS.
+//
+// Both tiled kernels read one LDS tile in two ways: as MFMA row operands
+// (ds_read_b128 of 16-byte chunks) and transposed (ds_read_b64_tr_b16).  The
+// swizzle stores chunk c of row r at c ^ (4 (r % 4) + (r / 4) % 4): sixteen
+// consecutive rows put one logical chunk on sixteen distinct chunks, and four
+// consecutive rows (a transposing read) spread four logical chunks over
+// sixteen.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fwd_common.hpp"
+
+namespace vdn {
+
+namespace {
+
+template <int CH>
+__device__ __forceinline__ int dual_swz(int r) {
+  return (4 * (r & 3) + ((r >> 2) & 3)) & (CH - 1);
+}
+
+// Per-row pass: one thread per (sample, token, head).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rows_kernel(const BwdArgs a, int64_t total) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;  // ((b * S) + i) * H + h
+  if (idx >= total) return;
+  const int h = int(idx % a.H);
+  const int64_t bi = idx / a.H;
+  const int i = int(bi % a.S);
+  const int b = int(bi / a.S);
+  const bf16x8* o = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.out) + idx * D);
+  const bf16x8* g = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.dout) + idx * D);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const bf16x8 x = o[c], y = g[c];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(float(x[e]), float(y[e]), acc);
+  }
+  float sgv = 1.f;
+  if (a.gate != nullptr) {
+    sgv = 1.f / (1.f + __builtin_amdgcn_exp2f(-a.gate[idx] * kLog2e));
+    a.dgate[idx] = acc * (1.f - sgv);
+  }
+  const int64_t r = (int64_t(b) * a.H + h) * a.S + i;
+  a.delta[r] = acc;
+  a.sg[r] = sgv;
+#endif
+}
+
+// Transposing fragment read: lanes of a 16-lane group point at rows
+// rbase + 4 hh + i/4 (and + 8 for the second read), columns col0 + 4 (i % 4),
+// so lane i receives column col0 + i of rows {4hh .. 4hh+3, 8+4hh .. 8+4hh+3}:
+// the MFMA A-operand layout matching a score-layout B operand.
+__device__ __forceinline__ bf16x8 tr_frag(const char* p_lo, const char* p_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p_lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup = NW waves x 32 query rows of one (sample, head, query
+// block), keys in steps of KT through a 2-stage LDS ring (as the forward).
+// Per step, in the transposed score layout (one query per lane):
+//   S^T  = K Q^T        (A = K rows from LDS, B = Q in registers)
+//   dP^T = V dO^T       (A = V rows from LDS, B = dO in registers)
+//   dS^T = P (sg dP - delta) scale, P = exp2(S c - lse log2 e)
+//   dQ^T += K^T dS^T    (A = K^T by transposing reads, B = dS^T packed to bf16)
+template <int D, int NW, int KT>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int QW = 32;
+  constexpr int M = NW * QW;
+  constexpr int RB = 2 * D;
+  constexpr int CH = D / 8;
+  constexpr int TILE = KT * RB;
+  constexpr int NI = TILE / 1024 / NW;
+  constexpr int RPI = 1024 / RB;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NKB = KT / 32;
+  static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
+  const BwdArgs& a = p.a;
+
+  __shared__ __attribute__((aligned(1024))) char Ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) char Ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs1[TILE];
+  auto kstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Ks0 : Ks1; };
+  auto vstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Vs0 : Vs1; };
+
+  const int w = blockIdx.x;
+  const int t = (w & 7) * p.per_xcd + (w >> 3);
+  if (t >= p.total_tiles) return;
+  const int bh = t / p.tiles_per_bh;
+  const int rank = t - bh * p.tiles_per_bh;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  int bi = 0;
+  while (bi + 1 < p.n_blocks && p.blk[bi + 1].tile_prefix <= rank) ++bi;
+  const KeyList kl = load_key_list(p.blk[bi]);
+  const int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
+  const int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  const int n_keys = kl.n_keys;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int hh = lane >> 5;
+
+  const int64_t rs = int64_t(a.H) * D;
+  const int64_t rsb = rs * 2;
+  const int64_t bh_off = int64_t(b) * a.S * rs + int64_t(h) * D;
+  const char* __restrict__ kg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.k) + bh_off);
+  const char* __restrict__ vg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.v) + bh_off);
+
+  // Q and dO rows of this wave (MFMA B operands), and the row's constants
+  const int lrow = wave * QW + lr;
+  const bool row_ok = lrow < rows;
+  bf16x8 qreg[NDS], oreg[NDS];
+  {
+    const int64_t off = bh_off + int64_t(row0 + lrow) * rs + hh * 8;
+    const __bf16* qs = static_cast<const __bf16*>(a.q) + off;
+    const __bf16* os = static_cast<const __bf16*>(a.dout) + off;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      qreg[ds] = row_ok ? *reinterpret_cast<const bf16x8*>(qs + ds * 16) : bf16x8{};
+      oreg[ds] = row_ok ? *reinterpret_cast<const bf16x8*>(os + ds * 16) : bf16x8{};
+    }
+  }
+  // P = exp2(S c - L); rows past the tile get L = +inf (P = 0)
+  float L = __builtin_inff(), sgs = 0.f, dls = 0.f;
+  if (row_ok) {
+    const int64_t r = (int64_t(b) * a.H + h) * a.S + row0 + lrow;
+    L = a.lse[r] * kLog2e;
+    sgs = a.sg[r] * a.scale;
+    dls = a.delta[r] * a.scale;
+  }
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  // DMA of K and V rows (swizzled), as in the forward
+  int dma_row[NI];
+  uint32_t goff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = wave * NI + i;
+    const int r = q * RPI + lane / CH;
+    const int pc = lane % CH;
+    dma_row[i] = r;
+    goff[i] = uint32_t(r * rsb + ((pc ^ dual_swz<CH>(r)) * 16));
+  }
+  auto issue = [&](int step, char* lbase, const char* gbase) {
+    const int j0 = step * KT;
+    const int iv_end = interval_end(kl, j0);
+    const int delta = interval_delta(kl, j0);
+    if (j0 + KT <= iv_end) {
+      const char* base = gbase + int64_t(j0 + delta) * rsb;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) lds_dma16(base, goff[i], lbase + (wave * NI + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int j = min(j0 + dma_row[i], n_keys - 1);
+        lds_dma16(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
+                  lbase + (wave * NI + i) * 1024);
+      }
+    }
+  };
+
+  // row-operand offsets: row lr (+32 kb), logical chunk 2 ds + hh
+  const uint32_t row_off0 = uint32_t(lr * RB + ((hh ^ dual_swz<CH>(lr)) * 16));
+  auto row_off = [&](int ds) { return row_off0 ^ uint32_t(32 * ds); };
+  // transposed-operand offsets: row 4 hh + i/4 (+ 8 for the second read),
+  // columns 32 db + 16 (g % 2) + 4 (i % 4); db XORs bits 6.. of the offset
+  uint32_t tr_off0[2];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = 4 * hh + (i >> 2) + 8 * rr;
+      const int col = 16 * (g & 1) + 4 * (i & 3);
+      tr_off0[rr] = uint32_t(row * RB + (((col >> 3) ^ dual_swz<CH>(row)) * 16) + (col & 7) * 2);
+    }
+  }
+
+  const float c = a.score_scale_log2;
+  const int nsteps = (n_keys + KT - 1) / KT;
+  const bool active = __builtin_amdgcn_readfirstlane(wave) * QW < rows;
+
+  // X^T = rows(X stage) * B^T for the KT keys of a stage (X = K or V)
+  auto rowprod = [&](const char* xs, const bf16x8 (&breg)[NDS], f32x16 (&s)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 x = *reinterpret_cast<const bf16x8*>(xs + kb * 32 * RB + row_off(ds));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, breg[ds], s[kb], 0, 0, 0);
+      }
+    }
+  };
+
+  auto body = [&](int step, auto st) {
+    constexpr int s_ = decltype(st)::value;
+    issue(step + 1, kstage(IC<1 - s_>{}), kg);
+    issue(step + 1, vstage(IC<1 - s_>{}), vg);
+    if (active) {
+      const char* ks = kstage(st);
+      f32x16 sc[NKB], dp[NKB];
+      rowprod(ks, qreg, sc);
+      rowprod(vstage(st), oreg, dp);
+      const int j0 = step * KT;
+      if (j0 + KT > n_keys) mask_tail<NKB>(sc, n_keys - j0, hh);
+      bf16x8 pk[NKB][2];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          bf16x8 v8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = half * 8 + e;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c, -L));
+            v8[e] = static_cast<__bf16>(pr * __builtin_fmaf(sgs, dp[kb][r], -dls));
+          }
+          pk[kb][half] = v8;
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const char* base = ks + (kb * 32 + half * 16) * RB;
+            const bf16x8 x = tr_frag(base + (tr_off0[0] ^ uint32_t(64 * db)), base + (tr_off0[1] ^ uint32_t(64 * db)));
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, pk[kb][half], acc[db], 0, 0, 0);
+          }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+  };
+
+  issue(0, Ks0, kg);
+  issue(0, Vs0, vg);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  for (int step = 0;;) {
+    body(step, IC<0>{});
+    if (++step >= nsteps) break;
+    body(step, IC<1>{});
+    if (++step >= nsteps) break;
+  }
+
+  if (row_ok) {
+    __bf16* dst = static_cast<__bf16*>(a.dq) + bh_off + int64_t(row0 + lrow) * rs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[db][g4 * 4 + r]);
+        *reinterpret_cast<bf16x4*>(dst + db * 32 + g4 * 8 + hh * 4) = o4;
+      }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: one workgroup = NW waves x 32 keys of one (sample, head, key
+// group); the query rows that see the group stream through a 2-stage LDS ring
+// in steps of QT rows.  Per 32-row block of a step, in the score layout (one
+// key per lane):
+//   S  = Q K^T      (A = Q rows from LDS, B = K in registers)
+//   dP = dO V^T     (A = dO rows from LDS, B = V in registers)
+//   P = exp2(S c - lse log2 e), dS = P (sg dP - delta)
+//   dV^T += dO^T (sg P),  dK^T += Q^T dS  (A by transposing reads; B packed)
+// One wave per SIMD: K, V and both accumulators live in registers.
+template <int D, int NW, int QT>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int KW = 32;          // keys per wave
+  constexpr int N = NW * KW;      // keys per workgroup
+  constexpr int RB = 2 * D;
+  constexpr int CH = D / 8;
+  constexpr int TILE = QT * RB;   // bytes per Q (or dO) stage
+  constexpr int NI = TILE / 1024 / NW;
+  constexpr int RPI = 1024 / RB;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  constexpr int NQB = QT / 32;    // 32-row blocks per step
+  static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
+  static_assert(NW >= 3 && QT <= 64, "three waves stage the per-row constants, one row per lane");
+  const BwdArgs& a = p.a;
+
+  __shared__ __attribute__((aligned(1024))) char Qs0[TILE];
+  __shared__ __attribute__((aligned(1024))) char Qs1[TILE];
+  __shared__ __attribute__((aligned(1024))) char Os0[TILE];
+  __shared__ __attribute__((aligned(1024))) char Os1[TILE];
+  __shared__ __attribute__((aligned(16))) float Rs[2][3][QT];  // per stage: L, delta, sg
+  auto qstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Qs0 : Qs1; };
+  auto ostage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Os0 : Os1; };
+
+  const int w = blockIdx.x;
+  const int t = (w & 7) * p.per_xcd + (w >> 3);
+  if (t >= p.total_tiles) return;
+  const int bh = t / p.tiles_per_bh;
+  const int rank = t - bh * p.tiles_per_bh;
+  const int b = bh / a.H;
+  const int h = bh - b * a.H;
+  int gi = 0;
+  while (gi + 1 < p.n_blocks && p.blk[gi + 1].tile_prefix <= rank) ++gi;
+  const KBlockDesc& kd = p.blk[gi];
+  KeyList kl;  // keys of the group
+  kl.n_keys = __builtin_amdgcn_readfirstlane(kd.n_keys);
+  kl.start1 = __builtin_amdgcn_readfirstlane(kd.kiv_start[0]);
+  kl.start2 = __builtin_amdgcn_readfirstlane(kd.kiv_start[1]);
+  kl.delta0 = __builtin_amdgcn_readfirstlane(kd.kiv_delta[0]);
+  kl.delta1 = __builtin_amdgcn_readfirstlane(kd.kiv_delta[1]);
+  kl.delta2 = __builtin_amdgcn_readfirstlane(kd.kiv_delta[2]);
+  KeyList rl;  // query rows that see them
+  rl.n_keys = __builtin_amdgcn_readfirstlane(kd.n_rows);
+  rl.start1 = __builtin_amdgcn_readfirstlane(kd.qiv_start);
+  rl.start2 = rl.n_keys;
+  rl.delta0 = __builtin_amdgcn_readfirstlane(kd.qiv_delta[0]);
+  rl.delta1 = __builtin_amdgcn_readfirstlane(kd.qiv_delta[1]);
+  rl.delta2 = 0;
+  const int key0 = (rank - kd.tile_prefix) * N;
+  const int n_rows = rl.n_keys;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int lr = lane & 31;
+  const int hh = lane >> 5;
+
+  const int64_t rs = int64_t(a.H) * D;
+  const int64_t rsb = rs * 2;
+  const int64_t bh_off = int64_t(b) * a.S * rs + int64_t(h) * D;
+  const char* __restrict__ qg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.q) + bh_off);
+  const char* __restrict__ og = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.dout) + bh_off);
+  const int64_t row_base = (int64_t(b) * a.H + h) * a.S;  // per-row arrays [B,H,S]
+
+  // this lane's key (B-operand column lr): K and V rows in registers
+  const int kj = key0 + wave * KW + lr;
+  const bool key_ok = kj < kl.n_keys;
+  const int ktok = vtoken(kl, min(kj, kl.n_keys - 1));
+  bf16x8 kreg[NDS], vreg[NDS];
+  {
+    const int64_t off = bh_off + int64_t(ktok) * rs + hh * 8;
+    const __bf16* ks = static_cast<const __bf16*>(a.k) + off;
+    const __bf16* vs = static_cast<const __bf16*>(a.v) + off;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      kreg[ds] = key_ok ? *reinterpret_cast<const bf16x8*>(ks + ds * 16) : bf16x8{};
+      vreg[ds] = key_ok ? *reinterpret_cast<const bf16x8*>(vs + ds * 16) : bf16x8{};
+    }
+  }
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+
+  // DMA of Q and dO rows (swizzled)
+  int dma_row[NI];
+  uint32_t goff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int q = wave * NI + i;
+    const int r = q * RPI + lane / CH;
+    const int pc = lane % CH;
+    dma_row[i] = r;
+    goff[i] = uint32_t(r * rsb + ((pc ^ dual_swz<CH>(r)) * 16));
+  }
+  auto issue = [&](int step, char* lbase, const char* gbase) {
+    const int i0 = step * QT;
+    const int iv_end = interval_end(rl, i0);
+    const int delta = interval_delta(rl, i0);
+    if (i0 + QT <= iv_end) {
+      const char* base = gbase + int64_t(i0 + delta) * rsb;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) lds_dma16(base, goff[i], lbase + (wave * NI + i) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int j = min(i0 + dma_row[i], n_rows - 1);
+        lds_dma16(gbase + int64_t(vtoken(rl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
+                  lbase + (wave * NI + i) * 1024);
+      }
+    }
+  };
+  // per-row constants of a step: waves 0, 1, 2 fetch L = lse log2 e, delta,
+  // sg for one row per lane (rows past the end: L = +inf, delta = sg = 0,
+  // which zeroes their weights)
+  auto fetch_rows = [&](int step) -> float {
+    const int i = step * QT + lane;
+    if (wave > 2 || lane >= QT) return 0.f;
+    if (i >= n_rows) return wave == 0 ? __builtin_inff() : 0.f;
+    const int64_t r = row_base + vtoken(rl, i);
+    if (wave == 0) return a.lse[r] * kLog2e;
+    return wave == 1 ? a.delta[r] : a.sg[r];
+  };
+  auto store_rows = [&](int stage, float x) {
+    if (wave <= 2 && lane < QT) Rs[stage][wave][lane] = x;
+  };
+
+  const uint32_t row_off0 = uint32_t(lr * RB + ((hh ^ dual_swz<CH>(lr)) * 16));
+  auto row_off = [&](int ds) { return row_off0 ^ uint32_t(32 * ds); };
+  uint32_t tr_off0[2];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = 4 * hh + (i >> 2) + 8 * rr;
+      const int col = 16 * (g & 1) + 4 * (i & 3);
+      tr_off0[rr] = uint32_t(row * RB + (((col >> 3) ^ dual_swz<CH>(row)) * 16) + (col & 7) * 2);
+    }
+  }
+
+  const float c = a.score_scale_log2;
+  const int nsteps = (n_rows + QT - 1) / QT;
+
+  auto body = [&](int step, auto st) {
+    constexpr int s_ = decltype(st)::value;
+    issue(step + 1, qstage(IC<1 - s_>{}), qg);
+    issue(step + 1, ostage(IC<1 - s_>{}), og);
+    const float nxt = fetch_rows(step + 1);
+    const char* qsb = qstage(st);
+    const char* osb = ostage(st);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+      const char* qs = qsb + qb * 32 * RB;
+      const char* os = osb + qb * 32 * RB;
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 xq = *reinterpret_cast<const bf16x8*>(qs + row_off(ds));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xq, kreg[ds], sc, 0, 0, 0);
+        const bf16x8 xo = *reinterpret_cast<const bf16x8*>(os + row_off(ds));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xo, vreg[ds], dp, 0, 0, 0);
+      }
+      // score register r holds query row 8 (r/4) + 4 hh + r % 4 of the block
+      bf16x8 pg[2], dsb[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int row = qb * 32 + 8 * g4 + 4 * hh;
+        const float4 Lr = *reinterpret_cast<const float4*>(&Rs[s_][0][row]);
+        const float4 Dr = *reinterpret_cast<const float4*>(&Rs[s_][1][row]);
+        const float4 Gr = *reinterpret_cast<const float4*>(&Rs[s_][2][row]);
+        const float Lv[4] = {Lr.x, Lr.y, Lr.z, Lr.w};
+        const float Dv[4] = {Dr.x, Dr.y, Dr.z, Dr.w};
+        const float Gv[4] = {Gr.x, Gr.y, Gr.z, Gr.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g4 + u;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -Lv[u]));
+          pg[r / 8][r % 8] = static_cast<__bf16>(pr * Gv[u]);
+          dsb[r / 8][r % 8] = static_cast<__bf16>(pr * __builtin_fmaf(Gv[u], dp[r], -Dv[u]));
+        }
+      }
+      // dV^T += dO^T (sg P), dK^T += Q^T dS over the block's two 16-row halves
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const char* ob = os + half * 16 * RB;
+        const char* qb2 = qs + half * 16 * RB;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const uint32_t x0 = tr_off0[0] ^ uint32_t(64 * db), x1 = tr_off0[1] ^ uint32_t(64 * db);
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(ob + x0, ob + x1), pg[half], dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(qb2 + x0, qb2 + x1), dsb[half], dk[db], 0, 0, 0);
+        }
+      }
+    }
+    store_rows(1 - s_, nxt);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
+  };
+
+  issue(0, Qs0, qg);
+  issue(0, Os0, og);
+  store_rows(0, fetch_rows(0));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
+  for (int step = 0;;) {
+    body(step, IC<0>{});
+    if (++step >= nsteps) break;
+    body(step, IC<1>{});
+    if (++step >= nsteps) break;
+  }
+
+  if (key_ok) {
+    const int64_t off = bh_off + int64_t(ktok) * rs;
+    __bf16* dkd = static_cast<__bf16*>(a.dk) + off;
+    __bf16* dvd = static_cast<__bf16*>(a.dv) + off;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        bf16x4 k4, v4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          k4[r] = static_cast<__bf16>(dk[db][g4 * 4 + r] * a.scale);
+          v4[r] = static_cast<__bf16>(dv[db][g4 * 4 + r]);
+        }
+        *reinterpret_cast<bf16x4*>(dkd + db * 32 + g4 * 8 + hh * 4) = k4;
+        *reinterpret_cast<bf16x4*>(dvd + db * 32 + g4 * 8 + hh * 4) = v4;
+      }
+  }
+#endif
+}
+
+constexpr int kDqWaves = 8;
+constexpr int kDqKeys = 64;
+constexpr int kKvWaves = 4;
+constexpr int kKvRows = 64;
+
+int bwd_dq_tile_m() { return 32 * kDqWaves; }
+int bwd_dkv_tile_n() { return 32 * kKvWaves; }
+
+int launch_bwd(const BwdDqParams& dq, const BwdKvParams& kv, int head_dim, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const BwdArgs& a = dq.a;
+  const int64_t total = int64_t(a.B) * a.S * a.H;
+  const dim3 rgrid(unsigned((total + 255) / 256));
+  const dim3 qgrid(unsigned(dq.per_xcd) * 8u), qblock(64 * kDqWaves);
+  const dim3 kgrid(unsigned(kv.per_xcd) * 8u), kblock(64 * kKvWaves);
+  if (head_dim == 128) {
+    hipLaunchKernelGGL((bwd_rows_kernel<128>), rgrid, dim3(256), 0, st, a, total);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, kDqWaves, kDqKeys>), qgrid, qblock, 0, st, dq);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128, kKvWaves, kKvRows>), kgrid, kblock, 0, st, kv);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL((bwd_rows_kernel<64>), rgrid, dim3(256), 0, st, a, total);
+    hipLaunchKernelGGL((bwd_dq_kernel<64, kDqWaves, kDqKeys>), qgrid, qblock, 0, st, dq);
+    hipLaunchKernelGGL((bwd_dkv_kernel<64, kKvWaves, kKvRows>), kgrid, kblock, 0, st, kv);
+  } else {
+    return int(hipErrorInvalidValue);
+  }
+  return int(hipGetLastError());
+}
+
+}  // namespace vdn

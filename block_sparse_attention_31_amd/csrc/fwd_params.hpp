@@ -1,4 +1,4 @@
-// Launch parameters shared by the C-ABI front end and the HIP forward kernels.
+// Launch parameters shared by the C-ABI front end and the HIP kernels.
 #pragma once
 
 #include <cstdint>
@@ -36,6 +36,62 @@ struct FwdParams {
   int32_t per_xcd;         // ceil(total_tiles / 8)
   QBlockDesc blk[kMaxQueryBlocks];
 };
+
+// ---- backward pass ----------------------------------------------------
+
+// A group of keys seen by the same query rows (the key side of the
+// structure), as the dK/dV kernel sees it.  Both lists are virtual
+// concatenations of token intervals in the KeyList form: virtual key j in
+// [kiv_start[i], kiv_start[i+1]) is token j + kiv_delta[i] (kiv_start[0] = 0,
+// unused starts = n_keys); likewise for the query rows with <= 2 intervals.
+struct KBlockDesc {
+  int32_t n_keys;
+  int32_t n_rows;
+  int32_t tile_prefix;  // tiles of the groups before this one in launch order
+  int32_t kiv_start[2];  // starts of key intervals 1 and 2
+  int32_t kiv_delta[3];
+  int32_t qiv_start;     // start of query interval 1
+  int32_t qiv_delta[2];
+};
+
+// Tensors and sizes shared by the backward kernels.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const void* dout;
+  const float* gate;   // [B,S,H] or nullptr
+  const float* lse;    // [B,H,S], natural log
+  float* delta;        // workspace [B,H,S]: sum_d dout * out
+  float* sg;           // workspace [B,H,S]: sigmoid(gate), 1 without a gate
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dgate;        // [B,S,H] or nullptr
+  int32_t B, S, H;
+  float scale;             // softmax scale
+  float score_scale_log2;  // scale * log2(e)
+};
+
+struct BwdDqParams {
+  BwdArgs a;
+  int32_t n_blocks, tiles_per_bh, total_tiles, per_xcd;
+  QBlockDesc blk[kMaxQueryBlocks];  // query blocks in launch order
+};
+
+struct BwdKvParams {
+  BwdArgs a;
+  int32_t n_blocks, tiles_per_bh, total_tiles, per_xcd;
+  KBlockDesc blk[kMaxQueryBlocks];  // key groups in launch order
+};
+
+// Query rows per dQ tile and keys per dK/dV tile.
+int bwd_dq_tile_m();
+int bwd_dkv_tile_n();
+
+// Enqueues the backward kernels (bf16 only): the per-row pass, dQ, dK/dV.
+int launch_bwd(const BwdDqParams& dq, const BwdKvParams& kv, int head_dim, void* stream);
 
 // Kernel-variant properties used by the front end.
 int kernel_tile_m(int head_dim, int dtype);

@@ -110,4 +110,49 @@ std::vector<Tile> tile_schedule(const std::vector<QueryBlock>& blocks, int tile_
   return out;
 }
 
+// Appends [lo, hi) to a canonical list being built in increasing order,
+// joining it with the previous interval when they touch.
+static void push_interval(Interval* iv, int* n, int64_t lo, int64_t hi) {
+  if (hi <= lo) return;
+  if (*n > 0 && lo <= iv[*n - 1].hi) {
+    iv[*n - 1].hi = std::max(iv[*n - 1].hi, hi);
+  } else {
+    iv[(*n)++] = {lo, hi};
+  }
+}
+
+std::vector<KeyBlock> build_key_blocks(const Geometry& g) {
+  std::vector<KeyBlock> out;
+  for (int64_t beta = 0; beta < g.nb; ++beta) {
+    // non-anchor frames of the block form one contiguous range: the anchors
+    // 0 and F-1 can only be its first or last frame
+    int64_t f0 = beta * g.Bf, f1 = std::min(g.F, (beta + 1) * g.Bf);
+    if (f0 == 0) f0 = 1;
+    if (f1 == g.F) f1 = g.F - 1;
+    if (f1 <= f0) continue;
+    KeyBlock kb;
+    push_interval(kb.kiv, &kb.n_kiv, f0 * g.T, f1 * g.T);
+    kb.n_keys = (f1 - f0) * g.T;
+    const int64_t lo = g.Bf * std::max<int64_t>(0, beta - 1);
+    const int64_t hi = std::min<int64_t>(g.F, g.Bf * (beta + 2));
+    push_interval(kb.qiv, &kb.n_qiv, lo * g.T, hi * g.T);
+    push_interval(kb.qiv, &kb.n_qiv, g.V, g.S);
+    kb.n_rows = 0;
+    for (int i = 0; i < kb.n_qiv; ++i) kb.n_rows += kb.qiv[i].hi - kb.qiv[i].lo;
+    out.push_back(kb);
+  }
+  KeyBlock gk;
+  push_interval(gk.kiv, &gk.n_kiv, 0, g.T);
+  if (g.F > 1) push_interval(gk.kiv, &gk.n_kiv, (g.F - 1) * g.T, g.V);
+  push_interval(gk.kiv, &gk.n_kiv, g.V, g.S);
+  gk.n_keys = 0;
+  for (int i = 0; i < gk.n_kiv; ++i) gk.n_keys += gk.kiv[i].hi - gk.kiv[i].lo;
+  if (gk.n_keys > 0) {
+    push_interval(gk.qiv, &gk.n_qiv, 0, g.S);
+    gk.n_rows = g.S;
+    out.push_back(gk);
+  }
+  return out;
+}
+
 }  // namespace vdn

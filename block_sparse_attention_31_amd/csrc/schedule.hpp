@@ -55,4 +55,22 @@ std::vector<int> cost_order(const std::vector<QueryBlock>& blocks);
 // Per-(sample, head) tile list in launch order.
 std::vector<Tile> tile_schedule(const std::vector<QueryBlock>& blocks, int tile_m);
 
+// The key side of the structure (gradients of the keys and values): a group
+// of keys seen by exactly the same query rows.  Keys of a frame block that
+// are not anchor frames are seen by the video rows of the block and its two
+// neighbours and by the text rows; anchor-frame keys and text keys are seen
+// by every row.
+struct KeyBlock {
+  int n_kiv = 0;
+  Interval kiv[kMaxIntervals];  // key tokens (canonical)
+  int64_t n_keys = 0;
+  int n_qiv = 0;
+  Interval qiv[kMaxIntervals];  // query rows that see them (canonical)
+  int64_t n_rows = 0;
+};
+
+// Key groups: frame blocks by index (their non-anchor frames; skipped when
+// empty), then the anchor and text keys (skipped when empty).
+std::vector<KeyBlock> build_key_blocks(const Geometry& g);
+
 }  // namespace vdn

@@ -129,6 +129,14 @@ def make_inputs(w: Workload) -> dict:
     return out
 
 
+def make_dout(w: Workload) -> torch.Tensor:
+    """Upstream gradient for the backward pass: bf16 [B, S, H, D], fp32
+    N(0,1) draws (seed + 2000) rounded to nearest even."""
+    rng = np.random.default_rng(w.seed + 2000)
+    x = rng.standard_normal((w.B, w.S, w.H, w.D), dtype=np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
 def random_workload(seed: int, **overrides) -> Workload:
     """A small seeded workload for sweeps (shape fields can be overridden)."""
     base = dict(name=f"rand{seed}", B=1, H=2, D=64, F=7, T=48, N=8, Bf=2,

@@ -101,6 +101,36 @@ int vdn_local_attn_fwd(const void* q, const void* k, const void* v,
                        float* lse, void* hip_stream);
 
 /*
+ * Backward pass (bf16 inputs only), asynchronous on `hip_stream`: the
+ * gradients of vdn_local_attn_fwd's output with respect to q, k, v and the
+ * gate logits, for an upstream gradient `dout`.  Derivative of the forward
+ * operation above (chain rule through the gate, the softmax and the two
+ * products).
+ *
+ *   q, k, v, gate, F .. block_frames, heads, head_dim, batch, softmax_scale
+ *             as for the forward (dtype VDN_BF16, head_dim 64 or 128).
+ *   out       device, [batch, S, heads, head_dim] bfloat16: the forward's
+ *             output for these inputs.
+ *   lse       device fp32 [batch, heads, S]: the forward's log-sum-exp.
+ *   dout      device, [batch, S, heads, head_dim] bfloat16.
+ *   dq, dk, dv device, [batch, S, heads, head_dim] bfloat16, written in full.
+ *   dgate     device fp32 [batch, S, heads], written in full; must be NULL
+ *             exactly when gate is NULL.
+ *   workspace device fp32, 2 * batch * heads * S floats of caller-owned
+ *             scratch (per-row constants); contents on return unspecified.
+ *
+ * Ownership and errors as for the forward: no allocation, no
+ * synchronisation, validation before any HIP call.  The outputs and the
+ * workspace must not overlap each other or any input.
+ */
+int vdn_local_attn_bwd(const void* q, const void* k, const void* v,
+                       const float* gate, const void* out, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv,
+                       float* dgate, int F, int tokens_per_frame, int n_text,
+                       int block_frames, int heads, int head_dim, int batch,
+                       float softmax_scale, float* workspace, void* hip_stream);
+
+/*
  * Host only.  Number of query blocks for a geometry: ceil(F/block_frames)
  * frame blocks, plus one text block when n_text > 0.  Returns the count
  * (>= 1) or a negative vdn_status_t.
@@ -143,6 +173,23 @@ int vdn_local_attn_count_pairs(int F, int tokens_per_frame, int n_text,
 int vdn_local_attn_tile_schedule(int F, int tokens_per_frame, int n_text,
                                  int block_frames, int tile_m, int32_t* out,
                                  int capacity, int* n_entries);
+
+/*
+ * Host only.  The key side of the structure, used by the backward pass: keys
+ * grouped by the query rows that see them (frame blocks by index with their
+ * non-anchor frames, skipped when empty; then the anchor-frame and text keys,
+ * skipped when empty):
+ *   key_intervals   [capacity][VDN_MAX_KEY_INTERVALS][2] int64: the group's
+ *                   keys, canonical as above, unused slots -1 (may be NULL);
+ *   query_intervals [capacity][VDN_MAX_KEY_INTERVALS][2] int64: the query
+ *                   rows that see every key of the group (may be NULL).
+ *   *n_kblocks      receives the number of groups.
+ * Returns VDN_ERR_CAPACITY (and sets *n_kblocks) if capacity is too small.
+ */
+int vdn_local_attn_key_blocks(int F, int tokens_per_frame, int n_text,
+                              int block_frames, int64_t* key_intervals,
+                              int64_t* query_intervals, int capacity,
+                              int* n_kblocks);
 
 /* Query rows per tile used by the forward kernel for a head_dim / dtype pair
  * (so callers can reproduce its schedule with vdn_local_attn_tile_schedule),

@@ -315,13 +315,17 @@ def _softmax_backward(p, dp):
 
 
 def attend_backward(q, k, v, gate, dout, F: int, T: int, N: int, Bf: int,
-                    scale: float | None = None, row_chunk: int = 2048):
+                    scale: float | None = None, row_chunk: int = 2048, rows=None, heads=None):
     """Gradients of :func:`attend` in fp64: returns (dq, dk, dv, dgate) with
     the shapes of q, k, v and gate (dgate is None without a gate).
 
     Query block by query block: recompute the softmax over the block's key set
     as the forward does, then apply the chain rule written out in the comment
-    above; the key gradients are scattered back to the gathered keys."""
+    above; the key gradients are scattered back to the gathered keys.
+
+    ``rows`` (sorted query indices) and ``heads`` restrict the work to a
+    sample: dq and dgate of those rows and heads are exact; dk and dv then only
+    hold the sampled rows' contributions."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -334,14 +338,22 @@ def attend_backward(q, k, v, gate, dout, F: int, T: int, N: int, Bf: int,
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dgate = None if gate is None else np.zeros((B, S, H))
+    heads = list(range(H)) if heads is None else list(heads)
     for (r0, r1), ivs in zip(query_blocks(F, T, N, Bf), key_intervals(F, T, N, Bf)):
+        if rows is None:
+            qrows = np.arange(r0, r1)
+        else:
+            rr = np.asarray(rows)
+            qrows = rr[(rr >= r0) & (rr < r1)]
+        if qrows.size == 0:
+            continue
         keys = np.concatenate([np.arange(a, b) for a, b in ivs])
         for b in range(B):
-            for h in range(H):
+            for h in heads:
                 kb = k[b, keys, h, :]
                 vb = v[b, keys, h, :]
-                for c0 in range(r0, r1, row_chunk):
-                    qi = np.arange(c0, min(r1, c0 + row_chunk))
+                for c0 in range(0, qrows.size, row_chunk):
+                    qi = qrows[c0:c0 + row_chunk]
                     s = (q[b, qi, h, :] @ kb.T) * scale
                     p, _ = _softmax_rows(s)
                     a = p @ vb

@@ -59,6 +59,11 @@ def test_key_intervals_bit_exact(L, F, T, N, Bf):
     assert B.vdn_local_attn_count_pairs(F, T, N, Bf) == oracle.count_pairs(F, T, N, Bf)
 
 
+@pytest.mark.parametrize("F,T,N,Bf", SWEEP)
+def test_key_blocks_bit_exact(L, F, T, N, Bf):
+    assert B.vdn_local_attn_key_blocks(F, T, N, Bf) == oracle.key_blocks(F, T, N, Bf)
+
+
 def test_golden_workloads(L, golden):
     for name, g in golden["workloads"].items():
         rows, ivs = B.vdn_local_attn_key_intervals(g["F"], g["T"], g["N"], g["Bf"])
@@ -172,3 +177,7 @@ def test_host_function_errors(L):
     n = ctypes.c_int(0)
     rc = L.vdn_local_attn_key_intervals(20, 10, 4, 5, None, None, 2, ctypes.byref(n))
     assert rc == -6 and n.value == 5
+    rc = L.vdn_local_attn_key_blocks(20, 10, 4, 5, None, None, 2, ctypes.byref(n))
+    assert rc == -6 and n.value == 5
+    with pytest.raises(B.VdnError):
+        B.vdn_local_attn_key_blocks(0, 4, 0, 5)

@@ -182,6 +182,16 @@ def test_key_gradients_sum_to_zero():
     assert np.max(np.abs(tot)) < 1e-10 * max(1.0, np.max(np.abs(dk)))
 
 
+def test_row_and_head_sampling_matches_full():
+    F, T, N, Bf, D = 12, 5, 4, 3, 8
+    q, k, v, g, do = _inputs(51, 2, 3, D, F, T, N, True)
+    full = oracle.attend_backward(q, k, v, g, do, F, T, N, Bf)
+    rows = np.array([0, 3, 14, 15, 31, 40, 59, 60, 63])
+    part = oracle.attend_backward(q, k, v, g, do, F, T, N, Bf, rows=rows, heads=[1, 2])
+    for x, y in ((full[0], part[0]), (full[3], part[3])):
+        np.testing.assert_allclose(x[:, rows][:, :, [1, 2]], y[:, rows][:, :, [1, 2]], rtol=1e-12, atol=1e-14)
+
+
 # ---------------------------------------------------------- mutation tests
 
 

@@ -1,0 +1,154 @@
+"""GPU parity of the HIP backward pass (through the C ABI) against the CPU
+oracle's gradients, on the same seeded inputs.
+
+The GPU forward supplies out and the log-sum-exp that the backward consumes;
+the oracle recomputes everything from the inputs in fp64.  Per gradient
+tensor the bar is a relative L2 error and a max-abs error in units of the
+reference's RMS (the gradients' scale varies by orders of magnitude between
+q/k, v and the gate, so absolute bars would not transfer)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_attention_31_amd import binding as B
+from block_sparse_attention_31_amd import synth
+
+from .gpu_util import gpu_available, oracle_inputs, sample_rows
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+# Each gradient element sums products of bf16-rounded factors (P, dS or
+# sg*P: relative 2^-9 each) with exact inputs in fp32, and is then rounded to
+# bf16 (2^-9); delta uses the bf16 forward output (2^-9).  A few 2^-9 relative
+# errors per summand: relative L2 error well under 1e-2, and no element off by
+# more than 2e-2 of the tensor's largest magnitude (2^-9 = 2e-3 per rounding,
+# times the summands' cancellation).
+REL_L2 = 1e-2
+MAX_OVER_PEAK = 2e-2
+
+
+def _log(name, stats):
+    print(f"[bwd-parity] {name}: " + ", ".join(f"{k}={v:.3g}" for k, v in stats.items()), flush=True)
+
+
+def run_bwd(inp, dout, w, scale=0.0):
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    gate = None if inp["gate"] is None else inp["gate"].to(dev)
+    do = dout.to(dev)
+    out, lse = B.local_attn_fwd(q, k, v, gate, F=w.F, tokens_per_frame=w.T, n_text=w.N,
+                                block_frames=w.Bf, softmax_scale=scale, return_lse=True)
+    grads = B.local_attn_bwd(q, k, v, gate, out, do, lse, F=w.F, tokens_per_frame=w.T, n_text=w.N,
+                             block_frames=w.Bf, softmax_scale=scale)
+    torch.cuda.synchronize()
+    return [None if t is None else t.cpu().to(torch.float64).numpy() for t in grads]
+
+
+def check(name, got, ref, heads=None):
+    stats = {}
+    for nm, g, r in zip(("dq", "dk", "dv", "dgate"), got, ref):
+        if r is None:
+            assert g is None
+            continue
+        if heads is not None:
+            g = g[:, :, heads]
+            r = r[:, :, heads]
+        assert np.all(np.isfinite(g)), nm
+        err = g - r
+        rms = math.sqrt(float(np.mean(r ** 2)))
+        rel = float(np.linalg.norm(err) / max(np.linalg.norm(r), 1e-30))
+        mx = float(np.max(np.abs(err)))
+        peak = float(np.max(np.abs(r)))
+        stats[f"{nm}_rel"] = rel
+        stats[f"{nm}_max/rms"] = mx / max(rms, 1e-30)
+        stats[f"{nm}_max/peak"] = mx / max(peak, 1e-30)
+        assert rel <= REL_L2, (name, nm, rel)
+        assert mx <= MAX_OVER_PEAK * peak, (name, nm, mx / peak)
+    _log(name, stats)
+    return stats
+
+
+def _oracle(inp, dout, w, scale=None):
+    q, k, v, g = oracle_inputs(inp)
+    return oracle.attend_backward(q, k, v, g, dout.to(torch.float64).numpy(), w.F, w.T, w.N, w.Bf,
+                                  scale=scale)
+
+
+def test_tiny_full():
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    check("tiny", run_bwd(inp, dout, w), _oracle(inp, dout, w))
+
+
+BWD_SHAPES = [
+    # B, H, D, F, T, N, Bf, gate
+    (1, 2, 64, 7, 48, 8, 2, True),
+    (2, 2, 128, 9, 37, 5, 2, True),      # ragged frames
+    (1, 2, 128, 1, 200, 0, 5, False),    # one frame (anchor only), no text
+    (1, 1, 128, 16, 64, 0, 5, True),     # no text
+    (1, 2, 128, 12, 130, 70, 3, False),
+    (1, 1, 64, 30, 5, 3, 1, True),       # one-frame blocks, tiny frames
+    (1, 1, 128, 6, 100, 300, 5, True),   # text block larger than a tile
+    (1, 1, 128, 5, 1, 1, 5, True),       # S = 6
+    (1, 1, 64, 11, 64, 16, 11, True),    # dense
+]
+
+
+@pytest.mark.parametrize("Bt,H,D,F,T,N,Bf,gate", BWD_SHAPES)
+def test_shapes_full(Bt, H, D, F, T, N, Bf, gate):
+    w = synth.random_workload(seed=300 + F * 7 + T, B=Bt, H=H, D=D, F=F, T=T, N=N, Bf=Bf, gate=gate)
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    check(f"B{Bt} H{H} D{D} F{F} T{T} N{N} Bf{Bf}", run_bwd(inp, dout, w), _oracle(inp, dout, w))
+
+
+def test_scale_and_outliers():
+    w = synth.random_workload(seed=377, B=1, H=2, D=128, F=10, T=40, N=12, Bf=5, gate=True,
+                              outlier_frac=0.02)
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    check("outliers, scale 0.05", run_bwd(inp, dout, w, scale=0.05), _oracle(inp, dout, w, scale=0.05))
+
+
+def test_medium_two_heads_full():
+    # the medium workload (S = 16512, 2% outlier channels), all gradients of
+    # two heads compared element by element
+    w = synth.WORKLOADS["medium"]
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    got = run_bwd(inp, dout, w)
+    heads = [0, 11]
+    idx = torch.tensor(heads)
+    sub = {n: inp[n].index_select(2, idx).contiguous() for n in ("q", "k", "v")}
+    sub["gate"] = inp["gate"].index_select(2, idx).contiguous()
+    sub["scales"] = None
+    ref = _oracle(sub, dout.index_select(2, idx).contiguous(), w)
+    check("medium heads 0,11", [None if g is None else g[:, :, heads] for g in got], ref)
+
+
+def test_768p_sampled():
+    # full 768p size: dq and dgate of sampled rows (every block edge, both
+    # sides of every 256-row dQ tile boundary, random rows) of four heads
+    # against the oracle, and every gradient finite.  dk and dv are compared
+    # element by element on the medium workload above (S = 16512) and on the
+    # small shapes; here the oracle would need every row of a key's query set.
+    w = synth.WORKLOADS["768p"]
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    dq, dk, dv, dg = run_bwd(inp, dout, w)
+    for t in (dq, dk, dv, dg):
+        assert np.all(np.isfinite(t))
+    rows = sample_rows(w, 256, 24, seed=7)
+    heads = [0, 9, 22, 31]
+    q, k, v, g = oracle_inputs(inp)
+    ref = oracle.attend_backward(q, k, v, g, dout.to(torch.float64).numpy(), w.F, w.T, w.N, w.Bf,
+                                 rows=rows, heads=heads)
+    sel = np.ix_(range(w.B), rows, heads)
+    check("768p sampled dq/dgate", [dq[sel], None, None, dg[sel]],
+          [ref[0][sel], None, None, ref[3][sel]])
