@@ -128,7 +128,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lr = lane & 31;
   const int hh = lane >> 5;
 
@@ -301,12 +301,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
 // in steps of QT rows.  Per 32-row block of a step, in the score layout (one
 // key per lane):
 //   S  = Q K^T      (A = Q rows from LDS, B = K in registers)
-//   dP = dO V^T     (A = dO rows from LDS, B = V in registers)
+//   dP = dO V^T     (A = dO rows from LDS, B = V rows from the LDS key tile)
 //   P = exp2(S c - lse log2 e), dS = P (sg dP - delta)
 //   dV^T += dO^T (sg P),  dK^T += Q^T dS  (A by transposing reads; B packed)
-// One wave per SIMD: K, V and both accumulators live in registers.
+// V of the workgroup's keys stays in LDS for the whole tile (read as B
+// operands), which keeps a wave within 256 registers: two waves per SIMD.
 template <int D, int NW, int QT>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p) {
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int KW = 32;          // keys per wave
   constexpr int N = NW * KW;      // keys per workgroup
@@ -318,6 +319,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int NQB = QT / 32;    // 32-row blocks per step
+  constexpr int NVI = KW * RB / 1024;  // DMA instructions per wave for its V rows
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
   static_assert(NW >= 3 && QT <= 64, "three waves stage the per-row constants, one row per lane");
   const BwdArgs& a = p.a;
@@ -326,6 +328,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
   __shared__ __attribute__((aligned(1024))) char Qs1[TILE];
   __shared__ __attribute__((aligned(1024))) char Os0[TILE];
   __shared__ __attribute__((aligned(1024))) char Os1[TILE];
+  __shared__ __attribute__((aligned(1024))) char Vt[N * RB];   // V rows of the tile's keys
   __shared__ __attribute__((aligned(16))) float Rs[2][3][QT];  // per stage: L, delta, sg
   auto qstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Qs0 : Qs1; };
   auto ostage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Os0 : Os1; };
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lr = lane & 31;
   const int hh = lane >> 5;
 
@@ -368,23 +371,30 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
   const int64_t bh_off = int64_t(b) * a.S * rs + int64_t(h) * D;
   const char* __restrict__ qg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.q) + bh_off);
   const char* __restrict__ og = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.dout) + bh_off);
+  const char* __restrict__ vg = reinterpret_cast<const char*>(static_cast<const __bf16*>(a.v) + bh_off);
   const int64_t row_base = (int64_t(b) * a.H + h) * a.S;  // per-row arrays [B,H,S]
 
-  // this lane's key (B-operand column lr): K and V rows in registers
+  // this lane's key (B-operand column lr): K row in registers
   const int kj = key0 + wave * KW + lr;
   const bool key_ok = kj < kl.n_keys;
   const int ktok = vtoken(kl, min(kj, kl.n_keys - 1));
-  bf16x8 kreg[NDS], vreg[NDS];
+  bf16x8 kreg[NDS];
   {
-    const int64_t off = bh_off + int64_t(ktok) * rs + hh * 8;
-    const __bf16* ks = static_cast<const __bf16*>(a.k) + off;
-    const __bf16* vs = static_cast<const __bf16*>(a.v) + off;
+    const __bf16* ks = static_cast<const __bf16*>(a.k) + bh_off + int64_t(ktok) * rs + hh * 8;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      kreg[ds] = key_ok ? *reinterpret_cast<const bf16x8*>(ks + ds * 16) : bf16x8{};
-      vreg[ds] = key_ok ? *reinterpret_cast<const bf16x8*>(vs + ds * 16) : bf16x8{};
-    }
+    for (int ds = 0; ds < NDS; ++ds) kreg[ds] = key_ok ? *reinterpret_cast<const bf16x8*>(ks + ds * 16) : bf16x8{};
   }
+  // V rows of this wave's keys into the key tile (keys past the group's end
+  // repeat its last key; their columns are never stored)
+  char* vt = Vt + wave * KW * RB;
+#pragma unroll
+  for (int i = 0; i < NVI; ++i) {
+    const int r = i * RPI + lane / CH;
+    const int pc = lane % CH;
+    const int tok = vtoken(kl, min(key0 + wave * KW + r, kl.n_keys - 1));
+    lds_dma16(vg + int64_t(tok) * rsb + (pc ^ dual_swz<CH>(r)) * 16, vt + i * 1024);
+  }
+
   f32x16 dk[NDB], dv[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -423,18 +433,21 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
   // per-row constants of a step: waves 0, 1, 2 fetch L = lse log2 e, delta,
   // sg for one row per lane (rows past the end: L = +inf, delta = sg = 0,
   // which zeroes their weights)
+  // (the value is used, and so waited for, only when stored at the end of
+  // the step: a wait right after the load would also drain the DMA)
+  const float* rsrc = (wave == 0 ? a.lse : wave == 1 ? a.delta : a.sg) + row_base;
   auto fetch_rows = [&](int step) -> float {
     const int i = step * QT + lane;
     if (wave > 2 || lane >= QT) return 0.f;
     if (i >= n_rows) return wave == 0 ? __builtin_inff() : 0.f;
-    const int64_t r = row_base + vtoken(rl, i);
-    if (wave == 0) return a.lse[r] * kLog2e;
-    return wave == 1 ? a.delta[r] : a.sg[r];
+    return rsrc[vtoken(rl, i)];
   };
   auto store_rows = [&](int stage, float x) {
-    if (wave <= 2 && lane < QT) Rs[stage][wave][lane] = x;
+    if (wave <= 2 && lane < QT) Rs[stage][wave][lane] = wave == 0 ? x * kLog2e : x;
   };
 
+  // row-operand offsets (row lr, logical chunk 2 ds + hh), for the streamed
+  // Q / dO blocks and for this wave's V rows alike
   const uint32_t row_off0 = uint32_t(lr * RB + ((hh ^ dual_swz<CH>(lr)) * 16));
   auto row_off = [&](int ds) { return row_off0 ^ uint32_t(32 * ds); };
   uint32_t tr_off0[2];
@@ -467,8 +480,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
       for (int ds = 0; ds < NDS; ++ds) {
         const bf16x8 xq = *reinterpret_cast<const bf16x8*>(qs + row_off(ds));
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xq, kreg[ds], sc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
         const bf16x8 xo = *reinterpret_cast<const bf16x8*>(os + row_off(ds));
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xo, vreg[ds], dp, 0, 0, 0);
+        const bf16x8 vb = *reinterpret_cast<const bf16x8*>(vt + row_off(ds));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xo, vb, dp, 0, 0, 0);
       }
       // score register r holds query row 8 (r/4) + 4 hh + r % 4 of the block
       bf16x8 pg[2], dsb[2];
@@ -510,7 +527,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
   issue(0, Qs0, qg);
   issue(0, Os0, og);
   store_rows(0, fetch_rows(0));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // V tile, step 0's rows
   lds_barrier();
   for (int step = 0;;) {
     body(step, IC<0>{});
@@ -542,8 +559,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dkv_kernel(const BwdKvParams p
 
 constexpr int kDqWaves = 8;
 constexpr int kDqKeys = 64;
-constexpr int kKvWaves = 4;
-constexpr int kKvRows = 64;
+constexpr int kKvWaves = 8;
 
 int bwd_dq_tile_m() { return 32 * kDqWaves; }
 int bwd_dkv_tile_n() { return 32 * kKvWaves; }
@@ -558,11 +574,11 @@ int launch_bwd(const BwdDqParams& dq, const BwdKvParams& kv, int head_dim, void*
   if (head_dim == 128) {
     hipLaunchKernelGGL((bwd_rows_kernel<128>), rgrid, dim3(256), 0, st, a, total);
     hipLaunchKernelGGL((bwd_dq_kernel<128, kDqWaves, kDqKeys>), qgrid, qblock, 0, st, dq);
-    hipLaunchKernelGGL((bwd_dkv_kernel<128, kKvWaves, kKvRows>), kgrid, kblock, 0, st, kv);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128, kKvWaves, 32>), kgrid, kblock, 0, st, kv);
   } else if (head_dim == 64) {
     hipLaunchKernelGGL((bwd_rows_kernel<64>), rgrid, dim3(256), 0, st, a, total);
     hipLaunchKernelGGL((bwd_dq_kernel<64, kDqWaves, kDqKeys>), qgrid, qblock, 0, st, dq);
-    hipLaunchKernelGGL((bwd_dkv_kernel<64, kKvWaves, kKvRows>), kgrid, kblock, 0, st, kv);
+    hipLaunchKernelGGL((bwd_dkv_kernel<64, kKvWaves, 64>), kgrid, kblock, 0, st, kv);
   } else {
     return int(hipErrorInvalidValue);
   }

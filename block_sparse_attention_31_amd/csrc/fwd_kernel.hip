@@ -112,7 +112,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lr = lane & 31;
   const int hh = lane >> 5;
 
