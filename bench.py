@@ -6,6 +6,8 @@ inputs already resident in HBM.  Prints one JSON line with effective TFLOP/s
 (allowed (query, key) pairs only: 4*D flops per pair per head), ms per step,
 the fraction of the dense MFMA peak, the speedup over the same kernel run
 dense (block_frames = F), and the CPU oracle timed on a bounded sample.
+Extra workloads (the fp8 forward, the backward pass) are reported under
+"other_workloads".
 
     python bench.py [--steps K] [--warmup W] [--workload 768p]
 """
@@ -99,8 +101,9 @@ def main() -> int:
     ap.add_argument("--workload", default="768p")
     ap.add_argument("--dense-steps", type=int, default=20, help="0 skips the dense run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
-    ap.add_argument("--also", default="768p-fp8",
-                    help="comma-separated extra workloads reported under 'other_workloads' ('' for none)")
+    ap.add_argument("--also", default="768p-fp8,768p-bwd",
+                    help="comma-separated extra workloads reported under 'other_workloads' "
+                         "(a '-bwd' suffix times the backward pass; '' for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -183,6 +186,49 @@ def main() -> int:
         }
         return w, inp, rec
 
+    def measure_bwd(name: str, steps: int, warmup: int):
+        """The backward pass of a workload (inputs, upstream gradient, and the
+        forward's out and log-sum-exp prepared outside the timed region)."""
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        gate = None if inp["gate"] is None else inp["gate"].to(dev)
+        dout = synth.make_dout(w).to(dev)
+        out, lse = binding.local_attn_fwd(q, k, v, gate, F=w.F, tokens_per_frame=w.T, n_text=w.N,
+                                          block_frames=w.Bf, return_lse=True)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        dgate = None if gate is None else torch.empty_like(gate)
+        ws = torch.empty(2 * w.B * w.H * w.S, dtype=torch.float32, device=dev)
+
+        def step():
+            binding.vdn_local_attn_bwd(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, w.F, w.T, w.N,
+                                       w.Bf, workspace=ws, stream=stream.cuda_stream)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        print(f"[bench] {w.name} backward: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
+        allowed, _ = binding.vdn_local_attn_count_pairs(w.F, w.T, w.N, w.Bf)
+        # 2.5x the forward's work: S recomputed, dP, dS K, dS^T Q, P^T dO
+        tflops = 10.0 * w.D * w.H * w.B * allowed / (ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[w.dtype]
+        return {"ms_per_step": round(ms, 4), "tflops": round(tflops, 2), "dtype": w.dtype,
+                "pass": "backward (dq, dk, dv, dgate)",
+                "flop_convention": "10*D per attended pair per head (2.5x forward)",
+                "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
+                           "frames": w.F, "tokens_per_frame": w.T, "text_tokens": w.N,
+                           "seq_len": w.S, "block_frames": w.Bf, "gate": w.gate},
+                "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
+                "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                             "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None}}
+
     w, inp, main_rec = measure(args.workload, args.steps, args.warmup, args.dense_steps)
     result = {
         "metric": METRIC,
@@ -206,8 +252,11 @@ def main() -> int:
     }
     others = {}
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
-        _, _, rec = measure(name, max(args.steps // 2, 5), max(args.warmup // 2, 2), 0)
-        others[name] = rec
+        if name.endswith("-bwd"):
+            others[name] = measure_bwd(name[:-4], max(args.steps // 5, 5), max(args.warmup // 5, 2))
+        else:
+            _, _, rec = measure(name, max(args.steps // 2, 5), max(args.warmup // 2, 2), 0)
+            others[name] = rec
     if others:
         result["other_workloads"] = others
     if args.cpu_seconds > 0:
