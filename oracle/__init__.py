@@ -1,4 +1,5 @@
-"""CPU fp64 oracle for the local Softmax branch of VDN-H3 hybrid video attention.
+"""CPU fp64 oracle for the local Softmax branch of VDN-H3 hybrid video attention
+(forward and backward), the complement linear branch and the fusion.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this package: only the tests, the smoke check and the benchmark's
@@ -23,6 +24,12 @@ values from the pages' description):
                                             finite differences, closed forms
                                             (constant values, zero queries,
                                             keys' gradients summing to zero)
+* ``linear_key_frames`` / ``linear_mask``  -- complement of the softmax
+                                            mask within video pairs, anchors
+                                            and window excluded
+* ``linear_branch``                      -- pair-by-pair sum over the explicit
+                                            mask, closed forms
+* ``phi``, ``rms_norm``, ``hybrid_fuse`` -- closed forms, torch routines
 
 No function here is "parity unpinned".
 """
@@ -39,6 +46,12 @@ from .local_attn import (  # noqa: F401
     attend_backward,
     attend_dense_masked,
     key_blocks,
+    phi,
+    linear_key_frames,
+    linear_mask,
+    linear_branch,
+    rms_norm,
+    hybrid_fuse,
     dequantize_fp8,
     sigmoid,
 )

@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle of the local Softmax branch of VDN-H3 attention.
+"""Plain fp64 CPU oracle of the local Softmax branch of VDN-H3 attention,
+its backward pass, the complement linear branch and the two-branch fusion.
 
 TEST INFRASTRUCTURE ONLY: used by tests, the smoke check and the benchmark's
 CPU-baseline leg.  Shares no code with the HIP path and imports nothing from
@@ -369,3 +370,107 @@ def attend_backward(q, k, v, gate, dout, F: int, T: int, N: int, Bf: int,
                     np.add.at(dk[b, :, h, :], keys, scale * (ds.T @ q[b, qi, h, :]))
                     np.add.at(dv[b, :, h, :], keys, p.T @ da)
     return dq, dk, dv, dgate
+
+
+# --------------------------------------------------------------------------
+# Complement linear branch and the two-branch fusion
+# --------------------------------------------------------------------------
+#
+# openi.cn "VDN-MiniMax-H3", technical principles: the linear branch sums up,
+# separately, what lies before and what lies after the current window, and
+# deliberately leaves out the window frames and the boundary anchors (so it
+# does not repeat the softmax branch); the same section: the linear branch's
+# output is RMS-normalised and then gated by its own content-dependent
+# sigmoid, and the two branches are summed.  nav.superapi.store
+# "VDN-MiniMax-H3 - OpenVDN's Open-Source Video Generation Acceleration
+# Solution", Technical Principles, "Hybrid Attention Architecture": long-range
+# linear attention with linear complexity.
+#
+# Readings (the pages fix neither the feature map nor the state update; the
+# frame-level normal-equation update they name is not specified and is left
+# out): plain linear attention with feature map phi(x) = elu(x) + 1 applied
+# elementwise to q and k; a video query of block beta uses the video keys of
+# frames outside [lo, hi) other than frames 0 and F-1; text queries get no
+# linear-branch output (zero), and text keys are not in the linear state
+# (writing text into the linear state is a separate mechanism the pages
+# name without defining).  Together with the softmax mask this covers every
+# (query, key) pair exactly once.  RMSNorm runs over a token's whole
+# linear-branch output (all heads), as the input of the branch's output
+# projection; the linear branch's gate is one logit per token and head.
+
+
+def phi(x):
+    """Linear-attention feature map elu(x) + 1 (positive everywhere)."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def linear_key_frames(beta: int, F: int, Bf: int) -> list[int]:
+    """Frames whose keys enter the linear branch of frame block ``beta``:
+    before and after the block window, anchors excluded."""
+    lo, hi = window_frames(beta, F, Bf)
+    return [f for f in range(F) if (f < lo or f >= hi) and f != 0 and f != F - 1]
+
+
+def linear_mask(F: int, T: int, N: int, Bf: int) -> np.ndarray:
+    """Explicit S x S mask of the linear branch, pair by pair from the rule
+    (video query, video key, key frame outside the query's window, key frame
+    not an anchor)."""
+    V = F * T
+    S = V + N
+    t = np.arange(S)
+    video = t < V
+    frame = np.where(video, t // max(T, 1), -1)
+    block = frame // Bf
+    lo = Bf * np.maximum(0, block - 1)
+    hi = np.minimum(F, Bf * (block + 2))
+    kf = frame[None, :]
+    outside = (kf < lo[:, None]) | (kf >= hi[:, None])
+    not_anchor = (kf != 0) & (kf != F - 1)
+    return video[:, None] & video[None, :] & outside & not_anchor
+
+
+def linear_branch(q, k, v, F: int, T: int, N: int, Bf: int):
+    """Linear-branch output in fp64, [B, S, H, D]: for a video query of block
+    beta, sum_j (phi(q_i).phi(k_j)) v_j / sum_j phi(q_i).phi(k_j) over the keys
+    of :func:`linear_key_frames`, computed through the summed state
+    sum_j phi(k_j) v_j^T and normaliser sum_j phi(k_j); zero for text queries
+    and for blocks with no such keys."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, H, D = q.shape
+    assert S == F * T + N, (S, F, T, N)
+    out = np.zeros((B, S, H, D))
+    for beta in range(num_frame_blocks(F, Bf)):
+        frames = linear_key_frames(beta, F, Bf)
+        if not frames:
+            continue
+        keys = np.concatenate([np.arange(f * T, (f + 1) * T) for f in frames])
+        r0, r1 = beta * Bf * T, min(F, (beta + 1) * Bf) * T
+        for b in range(B):
+            for h in range(H):
+                pk = phi(k[b, keys, h, :])
+                state = pk.T @ v[b, keys, h, :]      # D x D
+                z = pk.sum(axis=0)                   # D
+                pq = phi(q[b, r0:r1, h, :])
+                out[b, r0:r1, h, :] = (pq @ state) / (pq @ z)[:, None]
+    return out
+
+
+def rms_norm(x, weight, eps: float):
+    """RMSNorm of each token's whole branch output: x [B, S, H, D] is divided
+    by sqrt(mean over all H*D entries of x^2 + eps) and multiplied by
+    ``weight`` [H, D] (one weight per hidden channel)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = np.sqrt(np.mean(x * x, axis=(-2, -1), keepdims=True) + eps)
+    return x / r * np.asarray(weight, dtype=np.float64)[None, None]
+
+
+def hybrid_fuse(soft_out, lin_out, gate_lin, norm_weight, eps: float):
+    """The hybrid layer's attention output before the output projections:
+    the softmax-branch output (already multiplied by its own gate) plus the
+    RMS-normalised linear-branch output times the linear branch's sigmoid
+    gate (one logit per token and head, [B, S, H])."""
+    return (np.asarray(soft_out, dtype=np.float64)
+            + sigmoid(gate_lin)[..., None] * rms_norm(lin_out, norm_weight, eps))
