@@ -29,6 +29,7 @@ STATUS_NAMES = {
 
 # Every symbol the header declares, with (restype, argtypes).
 _i, _f, _p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+_i64 = ctypes.c_int64
 _pi64 = ctypes.POINTER(ctypes.c_int64)
 _pi32 = ctypes.POINTER(ctypes.c_int32)
 _pint = ctypes.POINTER(ctypes.c_int)
@@ -41,6 +42,9 @@ SIGNATURES = {
     "vdn_local_attn_tile_schedule": (_i, [_i, _i, _i, _i, _i, _pi32, _i, _pint]),
     "vdn_local_attn_key_blocks": (_i, [_i, _i, _i, _i, _pi64, _pi64, _i, _pint]),
     "vdn_local_attn_kernel_tile_m": (_i, [_i, _i]),
+    "vdn_linear_branch_fwd": (_i, [_p] * 4 + [_i] * 7 + [_p, _i64, _p]),
+    "vdn_linear_branch_workspace_bytes": (_i64, [_i] * 7),
+    "vdn_hybrid_fuse": (_i, [_p, _p, _p, _p, _f, _p, _i64, _i, _i, _p]),
     "vdn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -271,3 +275,84 @@ def local_attn_bwd(q, k, v, gate, out, dout, lse, *, F: int, tokens_per_frame: i
     vdn_local_attn_bwd(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, F, tokens_per_frame, n_text,
                        block_frames, softmax_scale=softmax_scale, workspace=ws)
     return dq, dk, dv, dgate
+
+
+# ------------------------------------------------ linear branch and fusion
+
+
+def vdn_linear_branch_workspace_bytes(F: int, tokens_per_frame: int, n_text: int, block_frames: int,
+                                      heads: int, head_dim: int, batch: int) -> int:
+    return _check(lib().vdn_linear_branch_workspace_bytes(F, tokens_per_frame, n_text, block_frames,
+                                                          heads, head_dim, batch))
+
+
+def vdn_linear_branch_fwd(q, k, v, out, F: int, tokens_per_frame: int, n_text: int,
+                          block_frames: int = 5, workspace=None, stream=None) -> None:
+    """Enqueue the linear branch on `stream` (default: torch's current stream).
+
+    q, k, v, out: [B, S, H, D] bf16 CUDA tensors; workspace: a CUDA tensor of
+    at least vdn_linear_branch_workspace_bytes(...) bytes."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    B, S, H, D = q.shape
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().vdn_linear_branch_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), F, tokens_per_frame, n_text, block_frames,
+        H, D, B, _ptr(workspace), nbytes, ctypes.c_void_p(stream))
+    _check(rc)
+
+
+def linear_branch_fwd(q, k, v, *, F: int, tokens_per_frame: int, n_text: int, block_frames: int = 5):
+    """Allocating convenience wrapper: returns the linear-branch output."""
+    import torch
+    B, S, H, D = q.shape
+    out = torch.empty_like(q)
+    nbytes = vdn_linear_branch_workspace_bytes(F, tokens_per_frame, n_text, block_frames, H, D, B)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    vdn_linear_branch_fwd(q, k, v, out, F, tokens_per_frame, n_text, block_frames, workspace=ws)
+    return out
+
+
+def vdn_hybrid_fuse(soft_out, lin_out, gate_lin, norm_weight, out, eps: float = 1e-6, stream=None) -> None:
+    """Enqueue the two-branch fusion on `stream`.
+
+    soft_out, lin_out, out: [..., H, D] bf16 CUDA tensors of one shape (out
+    may be soft_out); gate_lin [..., H] fp32; norm_weight [H, D] (or H*D) fp32."""
+    import torch
+    for name, t in (("soft_out", soft_out), ("lin_out", lin_out), ("out", out)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+        if t.shape != soft_out.shape:
+            raise ValueError(f"{name} must have the shape of soft_out")
+    if soft_out.dim() < 2:
+        raise ValueError("soft_out must be [..., heads, head_dim]")
+    H, D = soft_out.shape[-2], soft_out.shape[-1]
+    tokens = soft_out.numel() // (H * D)
+    for name, t, n in (("gate_lin", gate_lin, tokens * H), ("norm_weight", norm_weight, H * D)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a contiguous fp32 GPU tensor")
+        if t.numel() != n:
+            raise ValueError(f"{name} must hold {n} values, got {t.numel()}")
+    if tuple(gate_lin.shape) != tuple(soft_out.shape[:-1]):
+        raise ValueError(f"gate_lin must have shape {tuple(soft_out.shape[:-1])}")
+    if stream is None:
+        stream = torch.cuda.current_stream(soft_out.device).cuda_stream
+    rc = lib().vdn_hybrid_fuse(_ptr(soft_out), _ptr(lin_out), _ptr(gate_lin), _ptr(norm_weight),
+                               float(eps), _ptr(out), tokens, H, D, ctypes.c_void_p(stream))
+    _check(rc)
+
+
+def hybrid_fuse(soft_out, lin_out, gate_lin, norm_weight, eps: float = 1e-6):
+    """Allocating convenience wrapper: returns the fused output."""
+    import torch
+    out = torch.empty_like(soft_out)
+    vdn_hybrid_fuse(soft_out, lin_out, gate_lin, norm_weight, out, eps)
+    return out

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_NAME = "libvdn_local_attn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["api.cpp", "schedule.cpp", "fwd_kernel.hip", "fwd_fp8_kernel.hip", "bwd_kernel.hip"]
+SOURCES = ["api.cpp", "schedule.cpp", "fwd_kernel.hip", "fwd_fp8_kernel.hip", "bwd_kernel.hip", "linear_kernel.hip"]
 
 # Packed fp32 VALU instructions are disabled for all device code.
 HIP_FLAGS = [

@@ -11,6 +11,7 @@
 
 #include "../../include/vdn_local_attn.h"
 #include "fwd_params.hpp"
+#include "linear_params.hpp"
 #include "schedule.hpp"
 
 namespace {
@@ -397,6 +398,139 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
   kv_p.per_xcd = (kv_p.total_tiles + 7) / 8;
 
   const int rc = vdn::launch_bwd(dq_p, kv_p, head_dim, hip_stream);
+  if (rc != 0)
+    return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
+  return ok();
+}
+
+int64_t vdn_linear_branch_workspace_bytes(int F, int tokens_per_frame, int n_text, int block_frames,
+                                          int heads, int head_dim, int batch) {
+  vdn::Geometry g;
+  std::string err;
+  if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
+    return fail(VDN_ERR_INVALID_ARG, err);
+  if (heads <= 0 || batch <= 0) return fail(VDN_ERR_INVALID_ARG, "heads and batch must be >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(VDN_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got " + std::to_string(head_dim) + ")");
+  if (int64_t(batch) * heads > 65535) return fail(VDN_ERR_OVERFLOW, "batch * heads above 65535");
+  ok();
+  return int64_t(vdn::linear_workspace(batch, heads, g.F, g.nb, head_dim).total);
+}
+
+int vdn_linear_branch_fwd(const void* q, const void* k, const void* v, void* out, int F,
+                          int tokens_per_frame, int n_text, int block_frames, int heads,
+                          int head_dim, int batch, void* workspace, int64_t workspace_bytes,
+                          void* hip_stream) {
+  const int64_t need = vdn_linear_branch_workspace_bytes(F, tokens_per_frame, n_text, block_frames,
+                                                         heads, head_dim, batch);
+  if (need < 0) return int(need);
+  vdn::Geometry g;
+  std::string err;
+  vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err);
+  const void* need_ptr[] = {q, k, v, out, workspace};
+  for (const void* x : need_ptr)
+    if (x == nullptr) return fail(VDN_ERR_INVALID_ARG, "q, k, v, out and workspace must be non-NULL");
+  if (workspace_bytes < need)
+    return fail(VDN_ERR_INVALID_ARG, "workspace of " + std::to_string(workspace_bytes) + " bytes, " +
+                                         std::to_string(need) + " needed");
+  const void* a16[] = {q, k, v, out};
+  for (const void* x : a16)
+    if (!aligned(x, 16)) return fail(VDN_ERR_ALIGNMENT, "q, k, v and out must be 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(VDN_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (g.S > INT32_MAX / 2) return fail(VDN_ERR_OVERFLOW, "sequence length " + std::to_string(g.S) + " too large");
+  const int64_t elems = int64_t(batch) * g.S * int64_t(heads) * int64_t(head_dim);
+  if (elems / batch / heads / head_dim != g.S || elems > (int64_t(1) << 46))
+    return fail(VDN_ERR_OVERFLOW, "tensor element count overflows");
+  const size_t t_bytes = size_t(elems) * 2u;
+  const void* ins[] = {q, k, v};
+  for (const void* x : ins) {
+    if (overlaps(out, t_bytes, x, t_bytes)) return fail(VDN_ERR_INVALID_ARG, "out overlaps an input");
+    if (overlaps(workspace, size_t(need), x, t_bytes))
+      return fail(VDN_ERR_INVALID_ARG, "the workspace overlaps an input");
+  }
+  if (overlaps(workspace, size_t(need), out, t_bytes))
+    return fail(VDN_ERR_INVALID_ARG, "the workspace overlaps out");
+
+  vdn::LinParams p;
+  std::memset(&p, 0, sizeof(p));
+  const vdn::LinWorkspace w = vdn::linear_workspace(batch, heads, g.F, g.nb, head_dim);
+  char* ws = static_cast<char*>(workspace);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.fstate = reinterpret_cast<float*>(ws + w.fstate_off);
+  p.bstate = ws + w.bstate_off;
+  p.bz = reinterpret_cast<float*>(ws + w.bz_off);
+  p.B = batch;
+  p.S = int32_t(g.S);
+  p.H = heads;
+  p.F = int32_t(g.F);
+  p.T = int32_t(g.T);
+  p.Bf = int32_t(g.Bf);
+  p.nb = int32_t(g.nb);
+  const int64_t rt = vdn::kLinRowTile;
+  const int64_t full_rows = g.Bf * g.T;
+  const int64_t last_rows = (g.F - (g.nb - 1) * g.Bf) * g.T;
+  p.tiles_per_block = int32_t((full_rows + rt - 1) / rt);
+  p.tiles_last = int32_t((last_rows + rt - 1) / rt);
+  p.tiles_text = int32_t((g.N + rt - 1) / rt);
+  const int64_t per_bh = int64_t(p.tiles_per_block) * (g.nb - 1) + p.tiles_last + p.tiles_text;
+  const int64_t total = per_bh * batch * heads;
+  if (total > INT32_MAX / 2) return fail(VDN_ERR_OVERFLOW, "too many row tiles");
+  p.tiles_per_bh = int32_t(per_bh);
+  p.total_tiles = int32_t(total);
+  p.per_xcd = int32_t((total + 7) / 8);
+
+  const int rc = vdn::launch_linear(p, head_dim, hip_stream);
+  if (rc != 0)
+    return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
+  return ok();
+}
+
+int vdn_hybrid_fuse(const void* soft_out, const void* lin_out, const float* gate_lin,
+                    const float* norm_weight, float eps, void* out, int64_t tokens, int heads,
+                    int head_dim, void* hip_stream) {
+  if (tokens < 0 || heads <= 0 || head_dim <= 0)
+    return fail(VDN_ERR_INVALID_ARG, "tokens must be >= 0, heads and head_dim >= 1");
+  if (head_dim % 8 != 0)
+    return fail(VDN_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 (got " + std::to_string(head_dim) + ")");
+  const int64_t hd = int64_t(heads) * head_dim;
+  if (hd > 8192) return fail(VDN_ERR_UNSUPPORTED, "heads * head_dim above 8192");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(VDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const void* need_ptr[] = {soft_out, lin_out, gate_lin, norm_weight, out};
+  for (const void* x : need_ptr)
+    if (x == nullptr)
+      return fail(VDN_ERR_INVALID_ARG, "soft_out, lin_out, gate_lin, norm_weight and out must be non-NULL");
+  const void* a16[] = {soft_out, lin_out, norm_weight, out};
+  for (const void* x : a16)
+    if (!aligned(x, 16))
+      return fail(VDN_ERR_ALIGNMENT, "soft_out, lin_out, norm_weight and out must be 16-byte aligned");
+  if (!aligned(gate_lin, 4)) return fail(VDN_ERR_ALIGNMENT, "gate_lin must be 4-byte aligned");
+  if (tokens > (int64_t(1) << 40) / hd) return fail(VDN_ERR_OVERFLOW, "tokens * heads * head_dim too large");
+  if (tokens > int64_t(INT32_MAX) * 4 - 4) return fail(VDN_ERR_OVERFLOW, "too many tokens");
+  const size_t t_bytes = size_t(tokens * hd) * 2u;
+  const size_t g_bytes = size_t(tokens) * size_t(heads) * 4u;
+  const size_t w_bytes = size_t(hd) * 4u;
+  if (out != soft_out && overlaps(out, t_bytes, soft_out, t_bytes))
+    return fail(VDN_ERR_INVALID_ARG, "out overlaps soft_out without being the same buffer");
+  if (overlaps(out, t_bytes, lin_out, t_bytes) || overlaps(out, t_bytes, gate_lin, g_bytes) ||
+      overlaps(out, t_bytes, norm_weight, w_bytes))
+    return fail(VDN_ERR_INVALID_ARG, "out overlaps lin_out, gate_lin or norm_weight");
+  if (tokens == 0) return ok();
+
+  vdn::FuseParams p;
+  p.soft = soft_out;
+  p.lin = lin_out;
+  p.gate = gate_lin;
+  p.weight = norm_weight;
+  p.out = out;
+  p.rows = tokens;
+  p.H = heads;
+  p.D = head_dim;
+  p.HD = int32_t(hd);
+  p.eps = eps;
+  const int rc = vdn::launch_fuse(p, hip_stream);
   if (rc != 0)
     return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
   return ok();

@@ -34,11 +34,6 @@ namespace vdn {
 
 namespace {
 
-template <int CH>
-__device__ __forceinline__ int dual_swz(int r) {
-  return (4 * (r & 3) + ((r >> 2) & 3)) & (CH - 1);
-}
-
 // Per-row pass: one thread per (sample, token, head).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const BwdArgs a, int64_t total) {
@@ -67,16 +62,6 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const BwdArgs a, int64_t 
   a.delta[r] = acc;
   a.sg[r] = sgv;
 #endif
-}
-
-// Transposing fragment read: lanes of a 16-lane group point at rows
-// rbase + 4 hh + i/4 (and + 8 for the second read), columns col0 + 4 (i % 4),
-// so lane i receives column col0 + i of rows {4hh .. 4hh+3, 8+4hh .. 8+4hh+3}:
-// the MFMA A-operand layout matching a score-layout B operand.
-__device__ __forceinline__ bf16x8 tr_frag(const char* p_lo, const char* p_hi) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p_lo));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p_hi));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 }  // namespace

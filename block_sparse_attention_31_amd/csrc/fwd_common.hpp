@@ -1,4 +1,4 @@
-// Device helpers shared by the forward kernels (bf16 and fp8).
+// Device helpers shared by the attention kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -160,5 +160,27 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// LDS tile swizzle read both by rows (ds_read_b128 of 16-byte chunks) and
+// transposed (ds_read_b64_tr_b16): chunk c of row r sits at
+// c ^ (4 (r % 4) + (r / 4) % 4) (CH chunks per row).  Sixteen consecutive
+// rows put one logical chunk on sixteen distinct chunks, and four
+// consecutive rows (a transposing read) spread four logical chunks over
+// sixteen.  Period 16 in r.
+template <int CH>
+__device__ __forceinline__ int dual_swz(int r) {
+  return (4 * (r & 3) + ((r >> 2) & 3)) & (CH - 1);
+}
+
+// Transposing fragment read: lanes of a 16-lane group point at rows
+// rbase + 4 hh + i/4 (and + 8 for the second read), columns col0 + 4 (i % 4),
+// so lane i receives column col0 + i of rows {4hh .. 4hh+3, 8+4hh .. 8+4hh+3}:
+// the MFMA A-operand layout matching a score-layout B operand.
+__device__ __forceinline__ bf16x8 tr_frag(const char* p_lo, const char* p_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p_lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p_hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 
 }  // namespace vdn

@@ -1,0 +1,457 @@
+// Complement linear branch of VDN-H3 hybrid video attention, and the
+// two-branch fusion, for gfx950.
+//
+// The linear branch (openi.cn "VDN-MiniMax-H3", technical principles; the
+// complement of the local softmax window, summarising the frames before and
+// after a block's window, window frames and boundary anchors left out):
+// with phi(x) = elu(x) + 1, a video query i of frame block beta gets
+//   o_i = phi(q_i)^T S_beta / (phi(q_i) . z_beta),
+//   S_beta = sum_j phi(k_j) v_j^T,  z_beta = sum_j phi(k_j),
+// over the video keys j of frames f, 1 <= f <= F-2, outside the block's
+// window [lo, hi).  Text rows, and rows of a block with no such frame, get 0.
+//
+// Three kernels, all one pass over their inputs:
+//   1. frame states: per (sample, head, non-anchor frame), S_f^T = V_f^T
+//      phi(K_f) on bf16 MFMA with K and V staged through LDS by DMA and read
+//      back transposed, plus z_f = sum phi(k), to an fp32 workspace;
+//   2. block states: per state element, the sum over each block's frames
+//      (fp32, in frame order), written as bf16 S_beta^T and fp32 z_beta;
+//   3. apply: per (sample, head, row tile of one block), O^T = S_beta^T
+//      phi(Q)^T on bf16 MFMA with S_beta^T in LDS, the normaliser
+//      phi(q) . z_beta in fp32 on the vector ALUs.
+// The fusion (same page and section: the linear branch is RMS-normalised,
+// then gated by its own sigmoid gate, then added to the gated softmax
+// branch) is one wave per token over the token's H*D outputs.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "fwd_common.hpp"
+#include "linear_params.hpp"
+
+namespace vdn {
+
+namespace {
+
+// phi(x) = elu(x) + 1 = max(x, 0) + exp(min(x, 0)).
+[[maybe_unused]] __device__ __forceinline__ float phi(float x) {
+  return fmaxf(x, 0.f) + __builtin_amdgcn_exp2f(fminf(x, 0.f) * kLog2e);
+}
+
+// Number of non-anchor frames outside frame block beta's window.
+[[maybe_unused]] __device__ __forceinline__ int linear_frames(int beta, int F, int Bf) {
+  const int lo = Bf * max(0, beta - 1);
+  const int hi = min(F, Bf * (beta + 2));
+  return max(0, min(lo, F - 1) - 1) + max(0, (F - 1) - max(hi, 1));
+}
+
+// Waits until step s+1's DMA has landed when `ahead` later steps (0..2) are
+// also in flight, each `per` DMA instructions of this wave.
+template <int PER>
+__device__ __forceinline__ void wait_steps_ahead(int ahead) {
+  if (ahead >= 2)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
+  else if (ahead == 1)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+// ---------------------------------------------------------------------------
+// 1. Frame states.  One workgroup per (frame 1..F-2, sample * head); wave w
+// owns d1 columns [32w, 32w + 32) of S_f^T = sum_t v_t phi(k_t)^T, i.e. the
+// MFMA C[i = d2][j = d1] with A = V^T (transposing reads of the V tile) and
+// B = phi(K) (transposing reads of the K tile, phi applied in registers).
+// Both operands come from the same transposing read pattern, so their
+// k slots (token rows {4hh..4hh+3, 8+4hh..8+4hh+3} of a 16-row group) agree.
+template <int D, int NS>
+__global__ __launch_bounds__(D / 32 * 64) void lin_frame_state_kernel(const LinParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = D / 32;
+  constexpr int RB = 2 * D;
+  constexpr int CH = D / 8;
+  constexpr int KT = 32;                 // tokens per stage
+  constexpr int TILE = KT * RB;
+  constexpr int NI = TILE / 1024 / NW;   // DMA instructions per wave per tile
+  constexpr int RPI = 1024 / RB;
+  constexpr int NDB = D / 32;
+  static_assert(NI * NW * 1024 == TILE && NS >= 2 && NS <= 4, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char Ks[NS][TILE];
+  __shared__ __attribute__((aligned(1024))) char Vs[NS][TILE];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int f = 1 + int(blockIdx.x);
+  const int bh = int(blockIdx.y);
+  const int b = bh / p.H, h = bh % p.H;
+  const int T = p.T;
+  const int64_t rs = int64_t(p.H) * D;
+  const int64_t rsb = rs * 2;
+  const int64_t base = (int64_t(b) * p.S + int64_t(f) * T) * rs + int64_t(h) * D;
+  const char* __restrict__ kg = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.k) + base);
+  const char* __restrict__ vg = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.v) + base);
+  const int nsteps = (T + KT - 1) / KT;
+
+  int drow[NI];
+  uint32_t goff[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int r = (wave * NI + i) * RPI + lane / CH;
+    const int pc = lane % CH;
+    drow[i] = r;
+    goff[i] = uint32_t(r * rsb + ((pc ^ dual_swz<CH>(r)) * 16));
+  }
+  auto issue = [&](int step) {
+    if (step >= nsteps) return;
+    const int t0 = step * KT;
+    char* kl = Ks[step % NS];
+    char* vl = Vs[step % NS];
+    if (t0 + KT <= T) {
+      const char* kb = kg + int64_t(t0) * rsb;
+      const char* vb = vg + int64_t(t0) * rsb;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        lds_dma16(kb, goff[i], kl + (wave * NI + i) * 1024);
+        lds_dma16(vb, goff[i], vl + (wave * NI + i) * 1024);
+      }
+    } else {
+      // last, partial step: rows past the frame repeat its last token (their
+      // phi(k) is zeroed before use)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int t = min(t0 + drow[i], T - 1);
+        const int64_t off = int64_t(t) * rsb + (goff[i] - uint32_t(drow[i] * rsb));
+        lds_dma16(kg + off, kl + (wave * NI + i) * 1024);
+        lds_dma16(vg + off, vl + (wave * NI + i) * 1024);
+      }
+    }
+  };
+
+  uint32_t tr_off0[2];
+  {
+    const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int row = 4 * hh + (i >> 2) + 8 * rr;
+      const int col = 16 * (g & 1) + 4 * (i & 3);
+      tr_off0[rr] = uint32_t(row * RB + (((col >> 3) ^ dual_swz<CH>(row)) * 16) + (col & 7) * 2);
+    }
+  }
+  const uint32_t kx0 = tr_off0[0] ^ uint32_t(64 * wave), kx1 = tr_off0[1] ^ uint32_t(64 * wave);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  float zp = 0.f;
+
+  for (int s = 0; s < NS - 1; ++s) issue(s);
+  wait_steps_ahead<2 * NI>(min(NS - 2, nsteps - 1));
+  lds_barrier();
+  for (int step = 0; step < nsteps; ++step) {
+    issue(step + NS - 1);
+    const char* kl = Ks[step % NS];
+    const char* vl = Vs[step % NS];
+    const int rem = T - step * KT;  // valid tokens in this step (may exceed KT)
+#pragma unroll
+    for (int ks = 0; ks < KT / 16; ++ks) {
+      const char* kr = kl + ks * 16 * RB;
+      const char* vr = vl + ks * 16 * RB;
+      const bf16x8 kraw = tr_frag(kr + kx0, kr + kx1);
+      bf16x8 kb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x = phi(float(kraw[e]));
+        if (rem < KT) {
+          // token row 16 ks + 4 hh + e % 4 + 8 (e / 4) of the step
+          const float lim = float(rem - 16 * ks - 4 * hh - (e & 3) - 8 * (e >> 2)) - 0.5f;
+          x = __builtin_amdgcn_fmed3f(x, 0.f, lim * __builtin_inff());
+        }
+        kb[e] = static_cast<__bf16>(x);
+        zp += float(kb[e]);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint32_t x0 = tr_off0[0] ^ uint32_t(64 * db), x1 = tr_off0[1] ^ uint32_t(64 * db);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(vr + x0, vr + x1), kb, acc[db], 0, 0, 0);
+      }
+    }
+    wait_steps_ahead<2 * NI>(min(NS - 2, nsteps - 2 - step));
+    lds_barrier();
+  }
+
+  float* fs = p.fstate + (int64_t(bh) * (p.F - 2) + (f - 1)) * (D * D + D);
+  const int d1 = 32 * wave + (lane & 31);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d2 = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
+      fs[d2 * D + d1] = acc[db][r];
+    }
+  const float z = xhalf_sum(zp);
+  if (hh == 0) fs[D * D + d1] = z;
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// 2. Block states: one thread per state element (D*D entries of S^T, then D
+// of z) and sample * head; frames summed in order into up to 8 blocks per
+// pass.
+template <int D>
+__global__ __launch_bounds__(256) void lin_block_state_kernel(const LinParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int E = D * D + D;
+  const int e = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (e >= E) return;
+  const int bh = int(blockIdx.y);
+  const int nf = p.F - 2;
+  const float* src = p.fstate + int64_t(bh) * (nf > 0 ? nf : 0) * E + e;
+  for (int b0 = 0; b0 < p.nb; b0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    for (int f = 1; f <= nf; ++f) {
+      const float x = src[int64_t(f - 1) * E];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int beta = b0 + j;
+        const int lo = p.Bf * max(0, beta - 1);
+        const int hi = min(p.F, p.Bf * (beta + 2));
+        if (f < lo || f >= hi) acc[j] += x;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int beta = b0 + j;
+      if (beta >= p.nb) break;
+      const int64_t blk = int64_t(bh) * p.nb + beta;
+      if (e < D * D)
+        static_cast<__bf16*>(p.bstate)[blk * (D * D) + e] = static_cast<__bf16>(acc[j]);
+      else
+        p.bz[blk * D + (e - D * D)] = acc[j];
+    }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// 3. Apply.  One workgroup per (sample, head, tile of <= kLinRowTile rows of
+// one frame block, or of the text rows); workgroup ids are spread so that
+// consecutive tiles (sharing a block state) run on one XCD.  Each wave takes
+// 32-row groups: B = phi(Q)^T straight from global rows (16 bytes per lane),
+// A = S_beta^T rows from LDS, C[i = d2][j = row] holding one query per lane.
+template <int D>
+__global__ __launch_bounds__(256) void lin_apply_kernel(const LinParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NW = 4;
+  constexpr int RB = 2 * D;
+  constexpr int CH = D / 8;
+  constexpr int NDS = D / 16;
+  constexpr int NDB = D / 32;
+  __shared__ __attribute__((aligned(1024))) char Ss[D * RB];
+  __shared__ __attribute__((aligned(16))) float Zs[D];
+
+  const int xcd = int(blockIdx.x) % 8;
+  const int logical = xcd * p.per_xcd + int(blockIdx.x) / 8;
+  if (logical >= p.total_tiles) return;
+  const int bh = logical / p.tiles_per_bh;
+  const int tile = logical % p.tiles_per_bh;
+  const int b = bh / p.H, h = bh % p.H;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  const int lr = lane & 31;
+
+  const int V = p.F * p.T;
+  const int blk_rows = p.Bf * p.T;
+  const int tpb = p.tiles_per_block;
+  int beta, r_lo, r_hi;
+  if (tile < (p.nb - 1) * tpb) {
+    beta = tile / tpb;
+    r_lo = beta * blk_rows + (tile % tpb) * kLinRowTile;
+    r_hi = min(r_lo + kLinRowTile, (beta + 1) * blk_rows);
+  } else if (tile < (p.nb - 1) * tpb + p.tiles_last) {
+    beta = p.nb - 1;
+    r_lo = beta * blk_rows + (tile - (p.nb - 1) * tpb) * kLinRowTile;
+    r_hi = min(r_lo + kLinRowTile, V);
+  } else {
+    beta = -1;
+    r_lo = V + (tile - (p.nb - 1) * tpb - p.tiles_last) * kLinRowTile;
+    r_hi = min(r_lo + kLinRowTile, p.S);
+  }
+  const int64_t rs = int64_t(p.H) * D;
+  const int64_t bh_off = int64_t(b) * p.S * rs + int64_t(h) * D;
+  __bf16* __restrict__ og = static_cast<__bf16*>(p.out) + bh_off;
+
+  if (beta < 0 || linear_frames(beta, p.F, p.Bf) == 0) {
+    // text rows, or a block with no linear keys: zeros
+    const int n = (r_hi - r_lo) * CH;
+    for (int c = int(threadIdx.x); c < n; c += NW * 64) {
+      const int r = r_lo + c / CH;
+      *reinterpret_cast<u32x4*>(og + int64_t(r) * rs + (c % CH) * 8) = u32x4{0u, 0u, 0u, 0u};
+    }
+    return;
+  }
+
+  // block state into LDS (rows swizzled for row reads), normaliser too
+  {
+    const int64_t blk = int64_t(bh) * p.nb + beta;
+    const char* src = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.bstate) + blk * (D * D));
+#pragma unroll
+    for (int i = 0; i < D * CH / (NW * 64); ++i) {
+      const int c = int(threadIdx.x) + i * NW * 64;
+      const int r = c / CH, pc = c % CH;
+      *reinterpret_cast<u32x4*>(Ss + r * RB + ((pc ^ dual_swz<CH>(r)) * 16)) =
+          *reinterpret_cast<const u32x4*>(src + r * RB + pc * 16);
+    }
+    if (threadIdx.x < D) Zs[threadIdx.x] = p.bz[blk * D + threadIdx.x];
+  }
+  __syncthreads();
+
+  const __bf16* __restrict__ qg = static_cast<const __bf16*>(p.q) + bh_off;
+  const uint32_t row_off0 = uint32_t(lr * RB + ((hh ^ dual_swz<CH>(lr)) * 16));
+  const int ngroups = (r_hi - r_lo + 31) / 32;
+
+  auto load_q = [&](int g, bf16x8 (&qf)[NDS]) {
+    const int row = min(r_lo + 32 * g + lr, r_hi - 1);
+    const __bf16* src = qg + int64_t(row) * rs + 8 * hh;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = *reinterpret_cast<const bf16x8*>(src + 16 * ds);
+  };
+
+  bf16x8 qn[NDS];
+  int g = wave;
+  if (g < ngroups) load_q(g, qn);
+  for (; g < ngroups; g += NW) {
+    bf16x8 bq[NDS];
+    float den = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const float4 z0 = *reinterpret_cast<const float4*>(&Zs[16 * ds + 8 * hh]);
+      const float4 z1 = *reinterpret_cast<const float4*>(&Zs[16 * ds + 8 * hh + 4]);
+      const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bq[ds][e] = static_cast<__bf16>(phi(float(qn[ds][e])));
+        den = __builtin_fmaf(float(bq[ds][e]), zz[e], den);
+      }
+    }
+    if (g + NW < ngroups) load_q(g + NW, qn);
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      acc[db] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ss + db * 32 * RB + (row_off0 ^ uint32_t(32 * ds)));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ds], acc[db], 0, 0, 0);
+      }
+    }
+    den = xhalf_sum(den);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const int row = r_lo + 32 * g + lr;
+    if (row < r_hi) {
+      __bf16* dst = og + int64_t(row) * rs;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 o4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[db][4 * g4 + r] * inv);
+          *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hh) = o4;
+        }
+    }
+  }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// Fusion: one wave per token; lane l holds elements 512 c + 8 l .. +7 of the
+// token's H*D outputs (NCH * 512 >= H*D).
+//   out = soft + sigmoid(gate_h) * lin * weight / sqrt(mean(lin^2) + eps)
+template <int NCH>
+__global__ __launch_bounds__(256) void fuse_kernel(const FuseParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + wave;
+  if (row >= p.rows) return;
+  const int HD = p.HD;
+  const __bf16* lin = static_cast<const __bf16*>(p.lin) + row * HD;
+  const __bf16* soft = static_cast<const __bf16*>(p.soft) + row * HD;
+  __bf16* out = static_cast<__bf16*>(p.out) + row * HD;
+  bf16x8 lv[NCH];
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int e = 512 * c + 8 * lane;
+    lv[c] = e < HD ? *reinterpret_cast<const bf16x8*>(lin + e) : bf16x8{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(float(lv[c][i]), float(lv[c][i]), ss);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+  const float rinv = 1.f / __builtin_sqrtf(ss / float(HD) + p.eps);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int e = 512 * c + 8 * lane;
+    if (e < HD) {
+      const float g = p.gate[row * p.H + e / p.D];
+      const float sg = 1.f / (1.f + __builtin_amdgcn_exp2f(-g * kLog2e));
+      const float sc = sg * rinv;
+      const float4 w0 = *reinterpret_cast<const float4*>(p.weight + e);
+      const float4 w1 = *reinterpret_cast<const float4*>(p.weight + e + 4);
+      const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const bf16x8 s8 = *reinterpret_cast<const bf16x8*>(soft + e);
+      bf16x8 o8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o8[i] = static_cast<__bf16>(__builtin_fmaf(float(lv[c][i]) * ww[i], sc, float(s8[i])));
+      *reinterpret_cast<bf16x8*>(out + e) = o8;
+    }
+  }
+#endif
+}
+
+#ifndef VDN_LIN_NS
+#define VDN_LIN_NS 4
+#endif
+
+template <int D>
+int launch_linear_d(const LinParams& p, hipStream_t st) {
+  if (p.F > 2) {
+    hipLaunchKernelGGL((lin_frame_state_kernel<D, VDN_LIN_NS>), dim3(p.F - 2, p.B * p.H), dim3(D / 32 * 64), 0, st, p);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return int(e);
+  }
+  hipLaunchKernelGGL((lin_block_state_kernel<D>), dim3((D * D + D + 255) / 256, p.B * p.H), dim3(256), 0, st, p);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return int(e);
+  hipLaunchKernelGGL((lin_apply_kernel<D>), dim3(p.per_xcd * 8), dim3(256), 0, st, p);
+  return int(hipGetLastError());
+}
+
+}  // namespace
+
+int launch_linear(const LinParams& p, int head_dim, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64 ? launch_linear_d<64>(p, st) : launch_linear_d<128>(p, st);
+}
+
+int launch_fuse(const FuseParams& p, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(unsigned((p.rows + 3) / 4));
+  const int nch = (p.HD + 511) / 512;
+  if (nch <= 1)
+    hipLaunchKernelGGL((fuse_kernel<1>), grid, dim3(256), 0, st, p);
+  else if (nch <= 2)
+    hipLaunchKernelGGL((fuse_kernel<2>), grid, dim3(256), 0, st, p);
+  else if (nch <= 4)
+    hipLaunchKernelGGL((fuse_kernel<4>), grid, dim3(256), 0, st, p);
+  else if (nch <= 8)
+    hipLaunchKernelGGL((fuse_kernel<8>), grid, dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((fuse_kernel<16>), grid, dim3(256), 0, st, p);
+  return int(hipGetLastError());
+}
+
+}  // namespace vdn

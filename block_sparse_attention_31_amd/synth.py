@@ -154,3 +154,25 @@ def needle_queries(k: torch.Tensor, pairs, alpha: float) -> torch.Tensor:
     for b, i, h, j in pairs:
         q[b, i, h] = alpha * kf[b, j, h]
     return q.to(k.dtype)
+
+
+def with_frame_offsets(v: torch.Tensor, F: int, T: int, step: float) -> torch.Tensor:
+    """Values with a per-frame offset: token t of frame f gets step * f added
+    to every channel (text tokens get step * F); re-rounded to bf16.  Makes an
+    average over keys depend on which frames it covers, not only on how many."""
+    S = v.shape[1]
+    frame = torch.clamp(torch.arange(S) // T, max=F).to(torch.float32)
+    return (v.to(torch.float32) + step * frame[None, :, None, None]).to(torch.bfloat16)
+
+
+def make_fuse_inputs(w: Workload) -> dict:
+    """Inputs of the two-branch fusion for the workload's shape (seed + 3000):
+    soft_out and lin_out [B,S,H,D] bf16 N(0,1), gate_lin [B,S,H] fp32 N(0,1)
+    logits and norm_weight [H,D] fp32 drawn as 1 + 0.1 N(0,1)."""
+    rng = np.random.default_rng(w.seed + 3000)
+    shape = (w.B, w.S, w.H, w.D)
+    soft = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16)
+    lin = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16)
+    gate = torch.from_numpy(rng.standard_normal((w.B, w.S, w.H), dtype=np.float32))
+    weight = torch.from_numpy(1.0 + 0.1 * rng.standard_normal((w.H, w.D), dtype=np.float32))
+    return {"soft": soft, "lin": lin, "gate": gate, "weight": weight}

@@ -131,6 +131,82 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v,
                        float softmax_scale, float* workspace, void* hip_stream);
 
 /*
+ * Complement linear branch, forward (bf16), asynchronous on `hip_stream`.
+ * openi.cn "VDN-MiniMax-H3", section "technical principles: local exact,
+ * remote compressed": the linear branch summarises the context before and
+ * after a block's window, leaving out the window frames and the boundary
+ * anchors; nav.superapi.store "VDN-MiniMax-H3 - OpenVDN's Open-Source Video
+ * Generation Acceleration Solution", Technical Principles, "Hybrid Attention
+ * Architecture": long-range attention of linear cost.  Plain linear attention
+ * with the feature map phi(x) = elu(x) + 1 (the pages fix no feature map and
+ * do not define their frame-level state update; this is the plain form):
+ *
+ *   for a video query i of frame block b, with K_lin(b) the video tokens of
+ *   frames f, 1 <= f <= F-2, outside the window of blocks b-1..b+1,
+ *     out_i = sum_j (phi(q_i).phi(k_j)) v_j / sum_j phi(q_i).phi(k_j),
+ *   j over K_lin(b); out_i = 0 for text queries and when K_lin(b) is empty.
+ *   Together with vdn_local_attn_fwd's key sets this splits every
+ *   (query, key) pair between the two branches.
+ *
+ *   q, k, v   device, [batch, S, heads, head_dim] bfloat16, S = F*T + N.
+ *   out       device, same shape, bfloat16, written in full.
+ *   F .. block_frames, heads, batch  as for vdn_local_attn_fwd.
+ *   head_dim  64 or 128.  batch * heads <= 65535.
+ *   workspace device, caller-owned scratch of at least workspace_bytes >=
+ *             vdn_linear_branch_workspace_bytes(...) bytes, 256-byte aligned;
+ *             holds per-frame and per-block states; contents on return
+ *             unspecified.
+ *
+ * Internally the products run on bf16 MFMA with fp32 accumulation (phi(k),
+ * phi(q) and the per-block state are rounded to bf16; the normaliser stays
+ * fp32).  No allocation, no synchronisation, validation before any HIP call;
+ * out and the workspace must not overlap each other or an input.
+ */
+int vdn_linear_branch_fwd(const void* q, const void* k, const void* v,
+                          void* out, int F, int tokens_per_frame, int n_text,
+                          int block_frames, int heads, int head_dim, int batch,
+                          void* workspace, int64_t workspace_bytes,
+                          void* hip_stream);
+
+/* Host only.  Workspace bytes vdn_linear_branch_fwd needs for this shape
+ * (B*H*(F-2)*(D*D+D) fp32 frame states, B*H*nb*D*D bf16 block states and
+ * B*H*nb*D fp32 normalisers, each region rounded up to 256 bytes), or a
+ * negative vdn_status_t. */
+int64_t vdn_linear_branch_workspace_bytes(int F, int tokens_per_frame,
+                                          int n_text, int block_frames,
+                                          int heads, int head_dim, int batch);
+
+/*
+ * Two-branch fusion, asynchronous on `hip_stream` (openi.cn "VDN-MiniMax-H3",
+ * section "technical principles": the linear branch's output is
+ * RMS-normalised, then multiplied by its own content-dependent sigmoid gate,
+ * and the branches are added; the output projections that follow are not
+ * part of this call).  Per token t (a row of heads * head_dim values):
+ *
+ *   out[t] = soft_out[t] + sigmoid(gate_lin[t, h]) * lin_out[t]
+ *            * norm_weight / sqrt(mean(lin_out[t]^2) + eps),
+ *
+ * the mean over all heads * head_dim values of the token, h the head of each
+ * value.  soft_out is the softmax branch's output with its own gate already
+ * applied (vdn_local_attn_fwd with a gate).
+ *
+ *   soft_out, lin_out  device, [tokens, heads, head_dim] bfloat16.
+ *   gate_lin           device fp32 [tokens, heads] logits.
+ *   norm_weight        device fp32 [heads * head_dim].
+ *   out                device, [tokens, heads, head_dim] bfloat16; may be
+ *                      the soft_out buffer itself, otherwise must not overlap
+ *                      an input.
+ *   head_dim           a multiple of 8; heads * head_dim <= 8192.
+ *   eps                finite, >= 0.
+ * bf16 buffers and norm_weight 16-byte aligned, gate_lin 4-byte aligned.
+ * tokens == 0 is a no-op.  No allocation, no synchronisation.
+ */
+int vdn_hybrid_fuse(const void* soft_out, const void* lin_out,
+                    const float* gate_lin, const float* norm_weight, float eps,
+                    void* out, int64_t tokens, int heads, int head_dim,
+                    void* hip_stream);
+
+/*
  * Host only.  Number of query blocks for a geometry: ceil(F/block_frames)
  * frame blocks, plus one text block when n_text > 0.  Returns the count
  * (>= 1) or a negative vdn_status_t.

@@ -181,3 +181,96 @@ def test_host_function_errors(L):
     assert rc == -6 and n.value == 5
     with pytest.raises(B.VdnError):
         B.vdn_local_attn_key_blocks(0, 4, 0, 5)
+
+
+# ------------------------------------------------ linear branch and fusion
+
+
+def _up256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("F,T,N,Bf", SWEEP[::7])
+@pytest.mark.parametrize("H,D,batch", [(32, 128, 1), (2, 64, 3)])
+def test_linear_workspace_bytes(L, F, T, N, Bf, H, D, batch):
+    # the size the header states: fp32 frame states for frames 1..F-2, bf16
+    # block states and fp32 normalisers, each region rounded up to 256 bytes
+    nb = -(-F // Bf)
+    bh = batch * H
+    want = (_up256(bh * max(F - 2, 0) * (D * D + D) * 4) + _up256(bh * nb * D * D * 2)
+            + _up256(bh * nb * D * 4))
+    assert B.vdn_linear_branch_workspace_bytes(F, T, N, Bf, H, D, batch) == want
+
+
+def lin_args(**kw):
+    args = dict(q=A, k=A + STEP, v=A + 2 * STEP, out=A + 3 * STEP, F=20, T=1008, N=512, Bf=5,
+                H=32, D=128, batch=1, ws=A + 4 * STEP, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return args
+
+
+LIN_ERRORS = [
+    ("F=0", dict(F=0), -1),
+    ("heads=0", dict(H=0), -1),
+    ("head_dim 96", dict(D=96), -2),
+    ("batch*heads", dict(H=70000), -4),
+    ("q NULL", dict(q=None), -1),
+    ("out NULL", dict(out=None), -1),
+    ("workspace NULL", dict(ws=None), -1),
+    ("workspace small", dict(ws_bytes=1000), -1),
+    ("q misaligned", dict(q=A + 8), -3),
+    ("workspace misaligned", dict(ws=A + 4 * STEP + 16), -3),
+    ("out aliases k", dict(out=A + STEP), -1),
+    ("workspace inside v", dict(ws=A + 2 * STEP + 4096), -1),
+    ("workspace over out", dict(ws=A + 3 * STEP - 4096), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", LIN_ERRORS, ids=[c[0] for c in LIN_ERRORS])
+def test_linear_argument_errors(L, name, kw, code):
+    a = lin_args(**kw)
+    rc = L.vdn_linear_branch_fwd(a["q"], a["k"], a["v"], a["out"], a["F"], a["T"], a["N"], a["Bf"],
+                                 a["H"], a["D"], a["batch"], a["ws"], a["ws_bytes"], a["stream"])
+    assert rc == code, (name, rc, B.vdn_last_error())
+    assert B.vdn_last_error() != ""
+
+
+def fuse_args(**kw):
+    args = dict(soft=A, lin=A + STEP, gate=A + 2 * STEP, w=A + 3 * STEP, eps=1e-6, out=A + 4 * STEP,
+                tokens=20672, H=32, D=128, stream=None)
+    args.update(kw)
+    return args
+
+
+FUSE_ERRORS = [
+    ("tokens<0", dict(tokens=-1), -1),
+    ("heads=0", dict(H=0), -1),
+    ("head_dim 12", dict(D=12), -2),
+    ("too wide", dict(H=128, D=128), -2),
+    ("eps nan", dict(eps=float("nan")), -1),
+    ("eps<0", dict(eps=-1.0), -1),
+    ("gate NULL", dict(gate=None), -1),
+    ("weight NULL", dict(w=None), -1),
+    ("soft misaligned", dict(soft=A + 8), -3),
+    ("weight misaligned", dict(w=A + 3 * STEP + 4), -3),
+    ("gate misaligned", dict(gate=A + 2 * STEP + 2), -3),
+    ("out inside soft", dict(out=A + 4096), -1),
+    ("out aliases lin", dict(out=A + STEP), -1),
+    ("out over gate", dict(out=A + 2 * STEP - 4096), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", FUSE_ERRORS, ids=[c[0] for c in FUSE_ERRORS])
+def test_fuse_argument_errors(L, name, kw, code):
+    a = fuse_args(**kw)
+    rc = L.vdn_hybrid_fuse(a["soft"], a["lin"], a["gate"], a["w"], a["eps"], a["out"], a["tokens"],
+                           a["H"], a["D"], a["stream"])
+    assert rc == code, (name, rc, B.vdn_last_error())
+    assert B.vdn_last_error() != ""
+
+
+def test_fuse_zero_tokens_is_a_no_op(L):
+    # validation passes and nothing is launched
+    a = fuse_args(tokens=0)
+    rc = L.vdn_hybrid_fuse(a["soft"], a["lin"], a["gate"], a["w"], a["eps"], a["out"], 0, a["H"], a["D"], None)
+    assert rc == 0
