@@ -6,8 +6,9 @@ inputs already resident in HBM.  Prints one JSON line with effective TFLOP/s
 (allowed (query, key) pairs only: 4*D flops per pair per head), ms per step,
 the fraction of the dense MFMA peak, the speedup over the same kernel run
 dense (block_frames = F), and the CPU oracle timed on a bounded sample.
-Extra workloads (the fp8 forward, the backward pass) are reported under
-"other_workloads".
+Extra workloads (the fp8 forward, the backward pass, the complement linear
+branch, the two-branch fusion and the whole hybrid attention output) are
+reported under "other_workloads".
 
     python bench.py [--steps K] [--warmup W] [--workload 768p]
 """
@@ -28,6 +29,7 @@ METRIC = "effective TFLOP/s + ms/call, 768p-shaped local-window attn; % MFMA pea
 # Dense MFMA peaks of MI355X in TFLOP/s: 256 CUs x 2.4 GHz x 4096 (bf16) or
 # 8192 (fp8) flop per clock per CU; AMD quotes them as 2.5 and 5.0 PFLOP/s.
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = {"bf16": ["fwd_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"],
                   "fp8": ["fwd_fp8_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.json")
@@ -101,9 +103,10 @@ def main() -> int:
     ap.add_argument("--workload", default="768p")
     ap.add_argument("--dense-steps", type=int, default=20, help="0 skips the dense run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
-    ap.add_argument("--also", default="768p-fp8,768p-bwd",
+    ap.add_argument("--also", default="768p-fp8,768p-bwd,768p-linear,768p-fuse,768p-hybrid",
                     help="comma-separated extra workloads reported under 'other_workloads' "
-                         "(a '-bwd' suffix times the backward pass; '' for none)")
+                         "(suffixes: '-bwd' the backward pass, '-linear' the linear branch, "
+                         "'-fuse' the fusion, '-hybrid' softmax + linear + fusion; '' for none)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -229,6 +232,108 @@ def main() -> int:
                 "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                              "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None}}
 
+    def event_time(step, steps: int, warmup: int) -> float:
+        """Average ms per step between two events on the launch stream."""
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def shape_config(w):
+        return {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D, "frames": w.F,
+                "tokens_per_frame": w.T, "text_tokens": w.N, "seq_len": w.S, "block_frames": w.Bf}
+
+    def linear_bytes(w) -> int:
+        """Compulsory HBM bytes of the linear branch: K and V of frames
+        1..F-2 once, Q of the rows whose block has keys outside its window,
+        and every output row (bf16)."""
+        nb = -(-w.F // w.Bf)
+        rows_with_keys = 0
+        for beta in range(nb):
+            lo, hi = w.Bf * max(0, beta - 1), min(w.F, w.Bf * (beta + 2))
+            if any((f < lo or f >= hi) for f in range(1, w.F - 1)):
+                rows_with_keys += (min(w.F, (beta + 1) * w.Bf) - beta * w.Bf) * w.T
+        per_head = 2 * max(w.F - 2, 0) * w.T + rows_with_keys + w.S
+        return per_head * w.B * w.H * w.D * 2
+
+    def hbm_roofline(nbytes: int, ms: float) -> dict:
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+
+    def measure_linear(name: str, steps: int, warmup: int):
+        """The complement linear branch (three kernels per step)."""
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        out = torch.empty_like(q)
+        nws = binding.vdn_linear_branch_workspace_bytes(w.F, w.T, w.N, w.Bf, w.H, w.D, w.B)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+        def step():
+            binding.vdn_linear_branch_fwd(q, k, v, out, w.F, w.T, w.N, w.Bf, workspace=ws,
+                                          stream=stream.cuda_stream)
+        ms = event_time(step, steps, warmup)
+        print(f"[bench] {w.name} linear branch: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
+        nbytes = linear_bytes(w)
+        return {"ms_per_step": round(ms, 4), "dtype": "bf16",
+                "pass": "complement linear branch (frame states, block states, apply)",
+                "algorithmic_bytes": nbytes, "workspace_bytes": nws,
+                "config": shape_config(w), "roofline": hbm_roofline(nbytes, ms)}
+
+    def measure_fuse(name: str, steps: int, warmup: int):
+        """The two-branch fusion over every token of the workload."""
+        w = synth.WORKLOADS[name]
+        fi = synth.make_fuse_inputs(w)
+        soft, lin = fi["soft"].to(dev), fi["lin"].to(dev)
+        gate, weight = fi["gate"].to(dev), fi["weight"].to(dev)
+        out = torch.empty_like(soft)
+
+        def step():
+            binding.vdn_hybrid_fuse(soft, lin, gate, weight, out, 1e-6, stream=stream.cuda_stream)
+        ms = event_time(step, steps, warmup)
+        print(f"[bench] {w.name} fusion: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
+        tokens = w.B * w.S
+        nbytes = 3 * tokens * w.H * w.D * 2 + tokens * w.H * 4 + w.H * w.D * 4
+        return {"ms_per_step": round(ms, 4), "dtype": "bf16",
+                "pass": "fusion: soft + sigmoid(g) * RMSNorm(lin) * w",
+                "algorithmic_bytes": nbytes, "config": shape_config(w),
+                "roofline": hbm_roofline(nbytes, ms)}
+
+    def measure_hybrid(name: str, steps: int, warmup: int):
+        """The hybrid attention output of one layer before the output
+        projections: gated softmax branch, linear branch, fusion."""
+        w = synth.WORKLOADS[name]
+        inp = synth.make_inputs(w)
+        fi = synth.make_fuse_inputs(w)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        gate = inp["gate"].to(dev) if inp["gate"] is not None else None
+        gl, weight = fi["gate"].to(dev), fi["weight"].to(dev)
+        soft, lin = torch.empty_like(q), torch.empty_like(q)
+        nws = binding.vdn_linear_branch_workspace_bytes(w.F, w.T, w.N, w.Bf, w.H, w.D, w.B)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        st = stream.cuda_stream
+
+        def step():
+            binding.vdn_local_attn_fwd(q, k, v, gate, soft, w.F, w.T, w.N, w.Bf, stream=st)
+            binding.vdn_linear_branch_fwd(q, k, v, lin, w.F, w.T, w.N, w.Bf, workspace=ws, stream=st)
+            binding.vdn_hybrid_fuse(soft, lin, gl, weight, soft, 1e-6, stream=st)
+        ms = event_time(step, steps, warmup)
+        print(f"[bench] {w.name} hybrid layer attention: {ms:.4f} ms/step over {steps} steps",
+              file=sys.stderr, flush=True)
+        return {"ms_per_step": round(ms, 4), "dtype": "bf16",
+                "pass": "hybrid attention output: softmax branch + linear branch + fusion (in place)",
+                "config": shape_config(w),
+                "context": "whole-layer figures on the pages (332.5 / 192.1 / 125.3 ms per layer on "
+                           "one B200) include projections and other hardware; not a target"}
+
     w, inp, main_rec = measure(args.workload, args.steps, args.warmup, args.dense_steps)
     result = {
         "metric": METRIC,
@@ -254,6 +359,12 @@ def main() -> int:
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         if name.endswith("-bwd"):
             others[name] = measure_bwd(name[:-4], max(args.steps // 5, 5), max(args.warmup // 5, 2))
+        elif name.endswith("-linear"):
+            others[name] = measure_linear(name[:-7], args.steps, args.warmup)
+        elif name.endswith("-fuse"):
+            others[name] = measure_fuse(name[:-5], args.steps, args.warmup)
+        elif name.endswith("-hybrid"):
+            others[name] = measure_hybrid(name[:-7], max(args.steps // 2, 5), max(args.warmup // 2, 2))
         else:
             _, _, rec = measure(name, max(args.steps // 2, 5), max(args.warmup // 2, 2), 0)
             others[name] = rec

@@ -480,7 +480,6 @@ int vdn_linear_branch_fwd(const void* q, const void* k, const void* v, void* out
   if (total > INT32_MAX / 2) return fail(VDN_ERR_OVERFLOW, "too many row tiles");
   p.tiles_per_bh = int32_t(per_bh);
   p.total_tiles = int32_t(total);
-  p.per_xcd = int32_t((total + 7) / 8);
 
   const int rc = vdn::launch_linear(p, head_dim, hip_stream);
   if (rc != 0)

@@ -18,7 +18,7 @@
 //      (fp32, in frame order), written as bf16 S_beta^T and fp32 z_beta;
 //   3. apply: per (sample, head, row tile of one block), O^T = S_beta^T
 //      phi(Q)^T on bf16 MFMA with S_beta^T in LDS, the normaliser
-//      phi(q) . z_beta in fp32 on the vector ALUs.
+//      phi(q) . z_beta from the same products (z split into two bf16 rows).
 // The fusion (same page and section: the linear branch is RMS-normalised,
 // then gated by its own sigmoid gate, then added to the gated softmax
 // branch) is one wave per token over the token's H*D outputs.
@@ -28,6 +28,10 @@
 
 #include "fwd_common.hpp"
 #include "linear_params.hpp"
+
+#ifndef VDN_FUSE_NT
+#define VDN_FUSE_NT 1
+#endif
 
 namespace vdn {
 
@@ -45,13 +49,18 @@ namespace {
   return max(0, min(lo, F - 1) - 1) + max(0, (F - 1) - max(hi, 1));
 }
 
-// Waits until step s+1's DMA has landed when `ahead` later steps (0..2) are
-// also in flight, each `per` DMA instructions of this wave.
-template <int PER>
+// Waits until a step's DMA has landed while `ahead` later steps (clamped to
+// 0..MAXA) stay in flight, each PER DMA instructions of this wave.
+template <int PER, int MAXA>
 __device__ __forceinline__ void wait_steps_ahead(int ahead) {
-  if (ahead >= 2)
+  static_assert(MAXA <= 4 && PER * MAXA < 64, "vmcnt range");
+  if (MAXA >= 4 && ahead >= 4)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PER));
+  else if (MAXA >= 3 && ahead >= 3)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER));
+  else if (MAXA >= 2 && ahead >= 2)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER));
-  else if (ahead == 1)
+  else if (MAXA >= 1 && ahead >= 1)
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER));
   else
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -64,18 +73,17 @@ __device__ __forceinline__ void wait_steps_ahead(int ahead) {
 // B = phi(K) (transposing reads of the K tile, phi applied in registers).
 // Both operands come from the same transposing read pattern, so their
 // k slots (token rows {4hh..4hh+3, 8+4hh..8+4hh+3} of a 16-row group) agree.
-template <int D, int NS>
+template <int D, int NS, int KT>
 __global__ __launch_bounds__(D / 32 * 64) void lin_frame_state_kernel(const LinParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = D / 32;
   constexpr int RB = 2 * D;
   constexpr int CH = D / 8;
-  constexpr int KT = 32;                 // tokens per stage
-  constexpr int TILE = KT * RB;
+  constexpr int TILE = KT * RB;          // KT tokens per stage
   constexpr int NI = TILE / 1024 / NW;   // DMA instructions per wave per tile
   constexpr int RPI = 1024 / RB;
   constexpr int NDB = D / 32;
-  static_assert(NI * NW * 1024 == TILE && NS >= 2 && NS <= 4, "tile shape");
+  static_assert(NI * NW * 1024 == TILE && KT % 16 == 0 && NS >= 2 && NS <= 6, "tile shape");
   __shared__ __attribute__((aligned(1024))) char Ks[NS][TILE];
   __shared__ __attribute__((aligned(1024))) char Vs[NS][TILE];
 
@@ -143,42 +151,60 @@ __global__ __launch_bounds__(D / 32 * 64) void lin_frame_state_kernel(const LinP
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float zp = 0.f;
-
   for (int s = 0; s < NS - 1; ++s) issue(s);
-  wait_steps_ahead<2 * NI>(min(NS - 2, nsteps - 1));
+  wait_steps_ahead<2 * NI, NS - 2>(min(NS - 2, nsteps - 1));
   lds_barrier();
-  for (int step = 0; step < nsteps; ++step) {
-    issue(step + NS - 1);
-    const char* kl = Ks[step % NS];
-    const char* vl = Vs[step % NS];
-    const int rem = T - step * KT;  // valid tokens in this step (may exceed KT)
+  // one step: all K and V fragments of the step read first, then phi on
+  // the K fragments (rows past the frame zeroed on the partial last step),
+  // then the MFMAs.  z = sum_t phi(k_t) comes from one more product per
+  // 16 tokens, with an all-ones A operand (every row of zacc holds z).
+  const bf16x8 ones = {__bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f),
+                       __bf16(1.f), __bf16(1.f), __bf16(1.f), __bf16(1.f)};
+  f32x16 zacc = f32x16{};
+  auto compute = [&](const char* kl, const char* vl, int rem, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    constexpr int NKS = KT / 16;
+    bf16x8 kraw[NKS], va[NKS][NDB];
 #pragma unroll
-    for (int ks = 0; ks < KT / 16; ++ks) {
+    for (int ks = 0; ks < NKS; ++ks) {
       const char* kr = kl + ks * 16 * RB;
       const char* vr = vl + ks * 16 * RB;
-      const bf16x8 kraw = tr_frag(kr + kx0, kr + kx1);
+      kraw[ks] = tr_frag(kr + kx0, kr + kx1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        va[ks][db] = tr_frag(vr + (tr_off0[0] ^ uint32_t(64 * db)), vr + (tr_off0[1] ^ uint32_t(64 * db)));
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
       bf16x8 kb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        float x = phi(float(kraw[e]));
-        if (rem < KT) {
+        float x = phi(float(kraw[ks][e]));
+        if constexpr (TAIL) {
           // token row 16 ks + 4 hh + e % 4 + 8 (e / 4) of the step
           const float lim = float(rem - 16 * ks - 4 * hh - (e & 3) - 8 * (e >> 2)) - 0.5f;
           x = __builtin_amdgcn_fmed3f(x, 0.f, lim * __builtin_inff());
         }
         kb[e] = static_cast<__bf16>(x);
-        zp += float(kb[e]);
       }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint32_t x0 = tr_off0[0] ^ uint32_t(64 * db), x1 = tr_off0[1] ^ uint32_t(64 * db);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(vr + x0, vr + x1), kb, acc[db], 0, 0, 0);
-      }
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks][db], kb, acc[db], 0, 0, 0);
+      zacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, kb, zacc, 0, 0, 0);
     }
-    wait_steps_ahead<2 * NI>(min(NS - 2, nsteps - 2 - step));
+  };
+  auto step_end = [&](int step) {
+    wait_steps_ahead<2 * NI, NS - 2>(min(NS - 2, nsteps - 2 - step));
     lds_barrier();
+  };
+  // full steps in the loop; a partial last step (T % KT != 0) after it
+  const int nfull = T / KT;
+  for (int step = 0; step < nfull; ++step) {
+    issue(step + NS - 1);
+    compute(Ks[step % NS], Vs[step % NS], KT, IC<0>{});
+    step_end(step);
   }
+  if (nfull < nsteps) compute(Ks[nfull % NS], Vs[nfull % NS], T - nfull * KT, IC<1>{});
 
   float* fs = p.fstate + (int64_t(bh) * (p.F - 2) + (f - 1)) * (D * D + D);
   const int d1 = 32 * wave + (lane & 31);
@@ -189,8 +215,8 @@ __global__ __launch_bounds__(D / 32 * 64) void lin_frame_state_kernel(const LinP
       const int d2 = 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3);
       fs[d2 * D + d1] = acc[db][r];
     }
-  const float z = xhalf_sum(zp);
-  if (hh == 0) fs[D * D + d1] = z;
+  // zacc register 0 of lanes 0..31 is row 0 of the ones product: z[d1]
+  if (hh == 0) fs[D * D + d1] = zacc[0];
 #endif
 }
 
@@ -209,16 +235,25 @@ __global__ __launch_bounds__(256) void lin_block_state_kernel(const LinParams p)
   const float* src = p.fstate + int64_t(bh) * (nf > 0 ? nf : 0) * E + e;
   for (int b0 = 0; b0 < p.nb; b0 += 8) {
     float acc[8];
+    int lo[8], hi[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-    for (int f = 1; f <= nf; ++f) {
-      const float x = src[int64_t(f - 1) * E];
+    for (int j = 0; j < 8; ++j) {
+      acc[j] = 0.f;
+      lo[j] = p.Bf * max(0, b0 + j - 1);
+      hi[j] = min(p.F, p.Bf * (b0 + j + 2));
+    }
+    // frames in batches of 8 loads in flight together (indexes clamped to
+    // the last frame; a clamped frame adds nothing)
+    for (int f0 = 1; f0 <= nf; f0 += 8) {
+      float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int beta = b0 + j;
-        const int lo = p.Bf * max(0, beta - 1);
-        const int hi = min(p.F, p.Bf * (beta + 2));
-        if (f < lo || f >= hi) acc[j] += x;
+      for (int u = 0; u < 8; ++u) x[u] = src[int64_t(min(f0 + u, nf) - 1) * E];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = f0 + u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (f <= nf && (f < lo[j] || f >= hi[j])) acc[j] += x[u];
       }
     }
 #pragma unroll
@@ -237,26 +272,30 @@ __global__ __launch_bounds__(256) void lin_block_state_kernel(const LinParams p)
 
 // ---------------------------------------------------------------------------
 // 3. Apply.  One workgroup per (sample, head, tile of <= kLinRowTile rows of
-// one frame block, or of the text rows); workgroup ids are spread so that
-// consecutive tiles (sharing a block state) run on one XCD.  Each wave takes
+// one frame block, or of the text rows).  Each wave takes
 // 32-row groups: B = phi(Q)^T straight from global rows (16 bytes per lane),
-// A = S_beta^T rows from LDS, C[i = d2][j = row] holding one query per lane.
-template <int D>
-__global__ __launch_bounds__(256) void lin_apply_kernel(const LinParams p) {
+// A = rows of the LDS state, C[i = d2][j = row] holding one query per lane.
+// The LDS state has D rows of S^T plus a 32-row block whose rows 0 and 1
+// hold z in two bf16 parts (z_hi = bf16(z), z_lo = bf16(z - z_hi)) and the
+// rest zeros: its product gives the normaliser phi(q) . z with fp32
+// accumulation on the matrix cores, to about 2^-17 of z.
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void lin_apply_kernel(const LinParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NW = 4;
   constexpr int RB = 2 * D;
   constexpr int CH = D / 8;
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(1024))) char Ss[D * RB];
-  __shared__ __attribute__((aligned(16))) float Zs[D];
+  constexpr int SR = D + 32;  // LDS state rows
+  __shared__ __attribute__((aligned(1024))) char Ss[SR * RB];
 
-  const int xcd = int(blockIdx.x) % 8;
-  const int logical = xcd * p.per_xcd + int(blockIdx.x) / 8;
+  // heads fastest: the workgroups in flight together cover whole token
+  // rows (measured faster than keeping a block state's tiles on one XCD)
+  const int logical = int(blockIdx.x);
   if (logical >= p.total_tiles) return;
-  const int bh = logical / p.tiles_per_bh;
-  const int tile = logical % p.tiles_per_bh;
+  const int nbh = p.B * p.H;
+  const int bh = logical % nbh;
+  const int tile = logical / nbh;
   const int b = bh / p.H, h = bh % p.H;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -294,18 +333,32 @@ __global__ __launch_bounds__(256) void lin_apply_kernel(const LinParams p) {
     return;
   }
 
-  // block state into LDS (rows swizzled for row reads), normaliser too
+  // block state into LDS (rows swizzled for row reads), then the normaliser
+  // block
   {
     const int64_t blk = int64_t(bh) * p.nb + beta;
     const char* src = reinterpret_cast<const char*>(static_cast<const __bf16*>(p.bstate) + blk * (D * D));
-#pragma unroll
-    for (int i = 0; i < D * CH / (NW * 64); ++i) {
-      const int c = int(threadIdx.x) + i * NW * 64;
+    for (int c = int(threadIdx.x); c < D * CH; c += NW * 64) {
       const int r = c / CH, pc = c % CH;
       *reinterpret_cast<u32x4*>(Ss + r * RB + ((pc ^ dual_swz<CH>(r)) * 16)) =
           *reinterpret_cast<const u32x4*>(src + r * RB + pc * 16);
     }
-    if (threadIdx.x < D) Zs[threadIdx.x] = p.bz[blk * D + threadIdx.x];
+    const float* zsrc = p.bz + blk * D;
+    for (int c = int(threadIdx.x); c < 32 * CH; c += NW * 64) {
+      const int r = c / CH, pc = c % CH;
+      bf16x8 x{};
+      if (r < 2) {
+        const float4 z0 = *reinterpret_cast<const float4*>(zsrc + 8 * pc);
+        const float4 z1 = *reinterpret_cast<const float4*>(zsrc + 8 * pc + 4);
+        const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const __bf16 hi = static_cast<__bf16>(zz[e]);
+          x[e] = r == 0 ? hi : static_cast<__bf16>(zz[e] - float(hi));
+        }
+      }
+      *reinterpret_cast<bf16x8*>(Ss + (D + r) * RB + ((pc ^ dual_swz<CH>(r)) * 16)) = x;
+    }
   }
   __syncthreads();
 
@@ -314,54 +367,50 @@ __global__ __launch_bounds__(256) void lin_apply_kernel(const LinParams p) {
   const int ngroups = (r_hi - r_lo + 31) / 32;
 
   auto load_q = [&](int g, bf16x8 (&qf)[NDS]) {
-    const int row = min(r_lo + 32 * g + lr, r_hi - 1);
-    const __bf16* src = qg + int64_t(row) * rs + 8 * hh;
+    const __bf16* src = qg + int64_t(min(r_lo + 32 * g + lr, r_hi - 1)) * rs + 8 * hh;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) qf[ds] = *reinterpret_cast<const bf16x8*>(src + 16 * ds);
   };
-
+  // one 32-row group of Q ahead in registers
   bf16x8 qn[NDS];
-  int g = wave;
-  if (g < ngroups) load_q(g, qn);
-  for (; g < ngroups; g += NW) {
+  if (wave < ngroups) load_q(wave, qn);
+  for (int g = wave; g < ngroups; g += NW) {
+    const int row = r_lo + 32 * g + lr;
     bf16x8 bq[NDS];
-    float den = 0.f;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const float4 z0 = *reinterpret_cast<const float4*>(&Zs[16 * ds + 8 * hh]);
-      const float4 z1 = *reinterpret_cast<const float4*>(&Zs[16 * ds + 8 * hh + 4]);
-      const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bq[ds][e] = static_cast<__bf16>(phi(float(qn[ds][e])));
-        den = __builtin_fmaf(float(bq[ds][e]), zz[e], den);
-      }
-    }
+    for (int ds = 0; ds < NDS; ++ds) bq[ds] = qn[ds];
     if (g + NW < ngroups) load_q(g + NW, qn);
-    f32x16 acc[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      acc[db] = f32x16{};
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bq[ds][e] = static_cast<__bf16>(phi(float(bq[ds][e])));
+
+    // normaliser block first, then the output columns two blocks at a time
+    auto block = [&](int db) {
+      f32x16 acc = f32x16{};
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ss + db * 32 * RB + (row_off0 ^ uint32_t(32 * ds)));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ds], acc[db], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[ds], acc, 0, 0, 0);
       }
-    }
-    den = xhalf_sum(den);
+      return acc;
+    };
+    const f32x16 zacc = block(NDB);
+    const float den = xhalf_sum(zacc[0] + zacc[1]);
     const float inv = den > 0.f ? 1.f / den : 0.f;
-    const int row = r_lo + 32 * g + lr;
-    if (row < r_hi) {
-      __bf16* dst = og + int64_t(row) * rs;
+    __bf16* dst = og + int64_t(row) * rs;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDB; ++db) {
+      const f32x16 acc = block(db);
+      if (row < r_hi) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           bf16x4 o4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[db][4 * g4 + r] * inv);
+          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[4 * g4 + r] * inv);
           *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hh) = o4;
         }
+      }
     }
   }
 #endif
@@ -371,6 +420,26 @@ __global__ __launch_bounds__(256) void lin_apply_kernel(const LinParams p) {
 // Fusion: one wave per token; lane l holds elements 512 c + 8 l .. +7 of the
 // token's H*D outputs (NCH * 512 >= H*D).
 //   out = soft + sigmoid(gate_h) * lin * weight / sqrt(mean(lin^2) + eps)
+// The token rows stream through once (non-temporal loads and stores, so the
+// weight row, read by every token, stays cached); soft_out is loaded up
+// front with lin_out, before the reduction.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p) {
+#if VDN_FUSE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+template <typename T>
+__device__ __forceinline__ void stream_store(T x, T* p) {
+#if VDN_FUSE_NT
+  __builtin_nontemporal_store(x, p);
+#else
+  *p = x;
+#endif
+}
+
 template <int NCH>
 __global__ __launch_bounds__(256) void fuse_kernel(const FuseParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -379,17 +448,22 @@ __global__ __launch_bounds__(256) void fuse_kernel(const FuseParams p) {
   const int64_t row = int64_t(blockIdx.x) * 4 + wave;
   if (row >= p.rows) return;
   const int HD = p.HD;
-  const __bf16* lin = static_cast<const __bf16*>(p.lin) + row * HD;
-  const __bf16* soft = static_cast<const __bf16*>(p.soft) + row * HD;
-  __bf16* out = static_cast<__bf16*>(p.out) + row * HD;
-  bf16x8 lv[NCH];
-  float ss = 0.f;
+  const u32x4* lin = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.lin) + row * HD);
+  const u32x4* soft = reinterpret_cast<const u32x4*>(static_cast<const __bf16*>(p.soft) + row * HD);
+  u32x4* out = reinterpret_cast<u32x4*>(static_cast<__bf16*>(p.out) + row * HD);
+  u32x4 lraw[NCH], sraw[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
     const int e = 512 * c + 8 * lane;
-    lv[c] = e < HD ? *reinterpret_cast<const bf16x8*>(lin + e) : bf16x8{};
+    lraw[c] = e < HD ? stream_load(lin + e / 8) : u32x4{0u, 0u, 0u, 0u};
+    sraw[c] = e < HD ? stream_load(soft + e / 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float ss = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(float(lv[c][i]), float(lv[c][i]), ss);
+  for (int c = 0; c < NCH; ++c) {
+    const bf16x8 lv = __builtin_bit_cast(bf16x8, lraw[c]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = __builtin_fmaf(float(lv[i]), float(lv[i]), ss);
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
@@ -404,29 +478,37 @@ __global__ __launch_bounds__(256) void fuse_kernel(const FuseParams p) {
       const float4 w0 = *reinterpret_cast<const float4*>(p.weight + e);
       const float4 w1 = *reinterpret_cast<const float4*>(p.weight + e + 4);
       const float ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      const bf16x8 s8 = *reinterpret_cast<const bf16x8*>(soft + e);
+      const bf16x8 lv = __builtin_bit_cast(bf16x8, lraw[c]);
+      const bf16x8 s8 = __builtin_bit_cast(bf16x8, sraw[c]);
       bf16x8 o8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o8[i] = static_cast<__bf16>(__builtin_fmaf(float(lv[c][i]) * ww[i], sc, float(s8[i])));
-      *reinterpret_cast<bf16x8*>(out + e) = o8;
+      for (int i = 0; i < 8; ++i) o8[i] = static_cast<__bf16>(__builtin_fmaf(float(lv[i]) * ww[i], sc, float(s8[i])));
+      stream_store(__builtin_bit_cast(u32x4, o8), out + e / 8);
     }
   }
 #endif
 }
 
 #ifndef VDN_LIN_NS
-#define VDN_LIN_NS 4
+#define VDN_LIN_NS 2
+#endif
+#ifndef VDN_LIN_KT
+#define VDN_LIN_KT 32
+#endif
+#ifndef VDN_LIN_APPLY_NW
+#define VDN_LIN_APPLY_NW 8
 #endif
 
 template <int D>
 int launch_linear_d(const LinParams& p, hipStream_t st) {
   if (p.F > 2) {
-    hipLaunchKernelGGL((lin_frame_state_kernel<D, VDN_LIN_NS>), dim3(p.F - 2, p.B * p.H), dim3(D / 32 * 64), 0, st, p);
+    const dim3 fs_grid(p.F - 2, p.B * p.H);
+    hipLaunchKernelGGL((lin_frame_state_kernel<D, VDN_LIN_NS, VDN_LIN_KT>), fs_grid, dim3(D / 32 * 64), 0, st, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return int(e);
   }
   hipLaunchKernelGGL((lin_block_state_kernel<D>), dim3((D * D + D + 255) / 256, p.B * p.H), dim3(256), 0, st, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return int(e);
-  hipLaunchKernelGGL((lin_apply_kernel<D>), dim3(p.per_xcd * 8), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((lin_apply_kernel<D, VDN_LIN_APPLY_NW>), dim3(p.total_tiles), dim3(VDN_LIN_APPLY_NW * 64), 0, st, p);
   return int(hipGetLastError());
 }
 

@@ -24,7 +24,6 @@ struct LinParams {
   int32_t tiles_text;       // apply tiles of the text rows
   int32_t tiles_per_bh;     // sum of the three counts above
   int32_t total_tiles;      // tiles_per_bh * B * H
-  int32_t per_xcd;          // ceil(total_tiles / 8)
 };
 
 // Byte offsets of the three workspace regions and the total size.
