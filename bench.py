@@ -31,7 +31,8 @@ METRIC = "effective TFLOP/s + ms/call, 768p-shaped local-window attn; % MFMA pea
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = {"bf16": ["fwd_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"],
-                  "fp8": ["fwd_fp8_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"]}
+                  "fp8": ["fwd_fp8_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"],
+                  "linear": ["linear_kernel.hip", "linear_params.hpp", "fwd_common.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.json")
 
 
@@ -45,10 +46,12 @@ def kernel_source_hash(dtype: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(dtype: str, workload: str):
+def load_traffic(dtype: str, workload: str, kernel: str | None = None):
     """HBM bytes per launch measured with rocprofv3 counters, if they were
-    taken on the kernel source as it is now; otherwise None."""
-    path = TRAFFIC_FILE.format(kernel=f"fwd_{dtype}", workload=workload)
+    taken on the kernel source as it is now; otherwise None.  `dtype` picks
+    the source set ("bf16", "fp8", "linear"), `kernel` the file name part
+    (default fwd_<dtype>)."""
+    path = TRAFFIC_FILE.format(kernel=kernel or f"fwd_{dtype}", workload=workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -263,10 +266,10 @@ def main() -> int:
         per_head = 2 * max(w.F - 2, 0) * w.T + rows_with_keys + w.S
         return per_head * w.B * w.H * w.D * 2
 
-    def hbm_roofline(nbytes: int, ms: float) -> dict:
+    def hbm_roofline(nbytes: int, ms: float, traffic=None) -> dict:
         gbs = nbytes / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic}
 
     def measure_linear(name: str, steps: int, warmup: int):
         """The complement linear branch (three kernels per step)."""
@@ -286,7 +289,8 @@ def main() -> int:
         return {"ms_per_step": round(ms, 4), "dtype": "bf16",
                 "pass": "complement linear branch (frame states, block states, apply)",
                 "algorithmic_bytes": nbytes, "workspace_bytes": nws,
-                "config": shape_config(w), "roofline": hbm_roofline(nbytes, ms)}
+                "config": shape_config(w),
+                "roofline": hbm_roofline(nbytes, ms, load_traffic("linear", w.name, "linear"))}
 
     def measure_fuse(name: str, steps: int, warmup: int):
         """The two-branch fusion over every token of the workload."""
@@ -305,7 +309,7 @@ def main() -> int:
         return {"ms_per_step": round(ms, 4), "dtype": "bf16",
                 "pass": "fusion: soft + sigmoid(g) * RMSNorm(lin) * w",
                 "algorithmic_bytes": nbytes, "config": shape_config(w),
-                "roofline": hbm_roofline(nbytes, ms)}
+                "roofline": hbm_roofline(nbytes, ms, load_traffic("linear", w.name, "fuse"))}
 
     def measure_hybrid(name: str, steps: int, warmup: int):
         """The hybrid attention output of one layer before the output
