@@ -106,7 +106,7 @@ def main() -> int:
     ap.add_argument("--workload", default="768p")
     ap.add_argument("--dense-steps", type=int, default=20, help="0 skips the dense run")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
-    ap.add_argument("--also", default="768p-fp8,768p-bwd,768p-linear,768p-fuse,768p-hybrid",
+    ap.add_argument("--also", default="768p-fp8,768p-bwd,768p-linear,768p-fuse,768p-hybrid,768p-h4",
                     help="comma-separated extra workloads reported under 'other_workloads' "
                          "(suffixes: '-bwd' the backward pass, '-linear' the linear branch, "
                          "'-fuse' the fusion, '-hybrid' softmax + linear + fusion; '' for none)")

@@ -57,6 +57,9 @@ WORKLOADS = {
                      seed=31003),
     "768p-fp8": Workload("768p-fp8", B=1, H=32, D=128, F=20, T=1008, N=512,
                          dtype="fp8", outlier_frac=0.02, seed=31004),
+    # one GPU's share of the 768p shape when 8 GPUs split the 32 heads
+    "768p-h4": Workload("768p-h4", B=1, H=4, D=128, F=20, T=1008, N=512,
+                        seed=31006),
     "long": Workload("long", B=2, H=32, D=128, F=42, T=1008, N=512,
                      seed=31005, per_sample_seed=True),
 }

@@ -80,7 +80,7 @@ def test_outliers_and_scale():
 
 # ------------------------------------------- full-size workloads, sampled
 
-@pytest.mark.parametrize("name", ["medium", "768p", "long"])
+@pytest.mark.parametrize("name", ["medium", "768p", "768p-h4", "long"])
 def test_workload_sampled(name):
     w = synth.WORKLOADS[name]
     inp = synth.make_inputs(w)
