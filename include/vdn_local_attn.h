@@ -157,9 +157,10 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v,
  *             holds per-frame and per-block states; contents on return
  *             unspecified.
  *
- * Internally the products run on bf16 MFMA with fp32 accumulation (phi(k),
- * phi(q) and the per-block state are rounded to bf16; the normaliser stays
- * fp32).  No allocation, no synchronisation, validation before any HIP call;
+ * Internally the products run on bf16 MFMA with fp32 accumulation: phi(k),
+ * phi(q) and the per-block state are rounded to bf16; the normaliser sum of
+ * phi(k) is accumulated in fp32 and enters the final product as two bf16
+ * parts (hi + lo, about 2^-17 of its value).  No allocation, no synchronisation, validation before any HIP call;
  * out and the workspace must not overlap each other or an input.
  */
 int vdn_linear_branch_fwd(const void* q, const void* k, const void* v,

@@ -132,6 +132,26 @@ def test_medium_two_heads_full():
     check("medium heads 0,11", [None if g is None else g[:, :, heads] for g in got], ref)
 
 
+def test_long_video_sampled():
+    # two samples with their own seeds, 42 frames (nine blocks, the last of
+    # two frames): dq and dgate of sampled rows of two heads, every gradient
+    # finite
+    w = synth.WORKLOADS["long"]
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    dq, dk, dv, dg = run_bwd(inp, dout, w)
+    for t in (dq, dk, dv, dg):
+        assert np.all(np.isfinite(t))
+    rows = sample_rows(w, 256, 6, seed=9)
+    heads = [3, 30]
+    q, k, v, g = oracle_inputs(inp)
+    ref = oracle.attend_backward(q, k, v, g, dout.to(torch.float64).numpy(), w.F, w.T, w.N, w.Bf,
+                                 rows=rows, heads=heads)
+    sel = np.ix_(range(w.B), rows, heads)
+    check("long sampled dq/dgate", [dq[sel], None, None, dg[sel]],
+          [ref[0][sel], None, None, ref[3][sel]])
+
+
 def test_768p_sampled():
     # full 768p size: dq and dgate of sampled rows (every block edge, both
     # sides of every 256-row dQ tile boundary, random rows) of four heads
