@@ -206,6 +206,7 @@ __global__ __launch_bounds__(D / 32 * 64) void lin_frame_state_kernel(const LinP
   }
   if (nfull < nsteps) compute(Ks[nfull % NS], Vs[nfull % NS], T - nfull * KT, IC<1>{});
 
+
   float* fs = p.fstate + (int64_t(bh) * (p.F - 2) + (f - 1)) * (D * D + D);
   const int d1 = 32 * wave + (lane & 31);
 #pragma unroll
@@ -221,50 +222,65 @@ __global__ __launch_bounds__(D / 32 * 64) void lin_frame_state_kernel(const LinP
 }
 
 // ---------------------------------------------------------------------------
-// 2. Block states: one thread per state element (D*D entries of S^T, then D
-// of z) and sample * head; frames summed in order into up to 8 blocks per
-// pass.
+// 2. Block states: one thread per 4 consecutive state elements (D*D entries
+// of S^T, then D of z; D*D + D is a multiple of 4) and sample * head.  The
+// frames' values are loaded in batches of up to FB frames in flight together,
+// then summed in frame order into each block outside whose window they lie.
 template <int D>
 __global__ __launch_bounds__(256) void lin_block_state_kernel(const LinParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int E = D * D + D;
-  const int e = int(blockIdx.x) * 256 + int(threadIdx.x);
-  if (e >= E) return;
+  constexpr int E4 = E / 4;
+  constexpr int FB = 20;   // frames per load batch
+  constexpr int BB = 8;    // blocks per pass
+  static_assert(E % 4 == 0, "state size");
+  const int e4 = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (e4 >= E4) return;
   const int bh = int(blockIdx.y);
   const int nf = p.F - 2;
-  const float* src = p.fstate + int64_t(bh) * (nf > 0 ? nf : 0) * E + e;
-  for (int b0 = 0; b0 < p.nb; b0 += 8) {
-    float acc[8];
-    int lo[8], hi[8];
+  const float4* src = reinterpret_cast<const float4*>(p.fstate + int64_t(bh) * (nf > 0 ? nf : 0) * E) + e4;
+  for (int b0 = 0; b0 < p.nb; b0 += BB) {
+    float4 acc[BB];
+    int lo[BB], hi[BB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      acc[j] = 0.f;
+    for (int j = 0; j < BB; ++j) {
+      acc[j] = float4{0.f, 0.f, 0.f, 0.f};
       lo[j] = p.Bf * max(0, b0 + j - 1);
       hi[j] = min(p.F, p.Bf * (b0 + j + 2));
     }
-    // frames in batches of 8 loads in flight together (indexes clamped to
-    // the last frame; a clamped frame adds nothing)
-    for (int f0 = 1; f0 <= nf; f0 += 8) {
-      float x[8];
+    for (int f0 = 1; f0 <= nf; f0 += FB) {
+      float4 x[FB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = src[int64_t(min(f0 + u, nf) - 1) * E];
+      for (int u = 0; u < FB; ++u) x[u] = src[int64_t(min(f0 + u, nf) - 1) * E4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < FB; ++u) {
         const int f = f0 + u;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (f <= nf && (f < lo[j] || f >= hi[j])) acc[j] += x[u];
+        for (int j = 0; j < BB; ++j)
+          if (f <= nf && (f < lo[j] || f >= hi[j])) {
+            acc[j].x += x[u].x;
+            acc[j].y += x[u].y;
+            acc[j].z += x[u].z;
+            acc[j].w += x[u].w;
+          }
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < BB; ++j) {
       const int beta = b0 + j;
       if (beta >= p.nb) break;
       const int64_t blk = int64_t(bh) * p.nb + beta;
-      if (e < D * D)
-        static_cast<__bf16*>(p.bstate)[blk * (D * D) + e] = static_cast<__bf16>(acc[j]);
-      else
-        p.bz[blk * D + (e - D * D)] = acc[j];
+      const int e = 4 * e4;
+      if (e < D * D) {
+        bf16x4 v4;
+        v4[0] = static_cast<__bf16>(acc[j].x);
+        v4[1] = static_cast<__bf16>(acc[j].y);
+        v4[2] = static_cast<__bf16>(acc[j].z);
+        v4[3] = static_cast<__bf16>(acc[j].w);
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.bstate) + blk * (D * D) + e) = v4;
+      } else {
+        *reinterpret_cast<float4*>(p.bz + blk * D + (e - D * D)) = acc[j];
+      }
     }
   }
 #endif
@@ -495,6 +511,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(const FuseParams p) {
 #ifndef VDN_LIN_KT
 #define VDN_LIN_KT 32
 #endif
+
 #ifndef VDN_LIN_APPLY_NW
 #define VDN_LIN_APPLY_NW 8
 #endif
@@ -506,7 +523,7 @@ int launch_linear_d(const LinParams& p, hipStream_t st) {
     hipLaunchKernelGGL((lin_frame_state_kernel<D, VDN_LIN_NS, VDN_LIN_KT>), fs_grid, dim3(D / 32 * 64), 0, st, p);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return int(e);
   }
-  hipLaunchKernelGGL((lin_block_state_kernel<D>), dim3((D * D + D + 255) / 256, p.B * p.H), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((lin_block_state_kernel<D>), dim3(((D * D + D) / 4 + 255) / 256, p.B * p.H), dim3(256), 0, st, p);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return int(e);
   hipLaunchKernelGGL((lin_apply_kernel<D, VDN_LIN_APPLY_NW>), dim3(p.total_tiles), dim3(VDN_LIN_APPLY_NW * 64), 0, st, p);
   return int(hipGetLastError());

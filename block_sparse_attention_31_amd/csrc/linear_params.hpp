@@ -7,7 +7,10 @@
 namespace vdn {
 
 // Rows of one linear-branch apply tile (a tile never spans two frame blocks).
-constexpr int kLinRowTile = 512;
+#ifndef VDN_LIN_ROW_TILE
+#define VDN_LIN_ROW_TILE 256
+#endif
+constexpr int kLinRowTile = VDN_LIN_ROW_TILE;
 
 struct LinParams {
   const void* q;   // [B,S,H,D] bf16
