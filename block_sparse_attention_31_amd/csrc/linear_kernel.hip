@@ -32,6 +32,13 @@
 #ifndef VDN_FUSE_NT
 #define VDN_FUSE_NT 1
 #endif
+#ifndef VDN_LIN_APPLY_STAGE
+#define VDN_LIN_APPLY_STAGE 1
+#endif
+// waves per SIMD the apply kernel is compiled for (4: two workgroups per CU)
+#ifndef VDN_LIN_APPLY_MINW
+#define VDN_LIN_APPLY_MINW 4
+#endif
 
 namespace vdn {
 
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(256) void lin_block_state_kernel(const LinParams p)
 
 // ---------------------------------------------------------------------------
 // 3. Apply.  One workgroup per (sample, head, tile of <= kLinRowTile rows of
-// one frame block, or of the text rows).  Each wave takes
+// one frame block, or of the text rows), four waves.  Each wave takes
 // 32-row groups: B = phi(Q)^T straight from global rows (16 bytes per lane),
 // A = rows of the LDS state, C[i = d2][j = row] holding one query per lane.
 // The LDS state has D rows of S^T plus a 32-row block whose rows 0 and 1
@@ -296,7 +303,7 @@ __global__ __launch_bounds__(256) void lin_block_state_kernel(const LinParams p)
 // rest zeros: its product gives the normaliser phi(q) . z with fp32
 // accumulation on the matrix cores, to about 2^-17 of z.
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void lin_apply_kernel(const LinParams p) {
+__global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(const LinParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int RB = 2 * D;
   constexpr int CH = D / 8;
@@ -304,6 +311,10 @@ __global__ __launch_bounds__(NW * 64) void lin_apply_kernel(const LinParams p) {
   constexpr int NDB = D / 32;
   constexpr int SR = D + 32;  // LDS state rows
   __shared__ __attribute__((aligned(1024))) char Ss[SR * RB];
+#if VDN_LIN_APPLY_STAGE
+  // per-wave output staging: 32 rows x 128 bytes (two 32-column blocks)
+  __shared__ __attribute__((aligned(16))) char Os[NW][32 * 128];
+#endif
 
   // heads fastest: the workgroups in flight together cover whole token
   // rows (measured faster than keeping a block state's tiles on one XCD)
@@ -414,6 +425,36 @@ __global__ __launch_bounds__(NW * 64) void lin_apply_kernel(const LinParams p) {
     const f32x16 zacc = block(NDB);
     const float den = xhalf_sum(zacc[0] + zacc[1]);
     const float inv = den > 0.f ? 1.f / den : 0.f;
+#if VDN_LIN_APPLY_STAGE
+    // the result layout holds one row per lane; the rows go out through LDS
+    // so that every store instruction writes whole 128-byte lines (8 rows x
+    // 128 bytes).  16-byte chunk c of a staged row sits at c ^ ((row/2) % 8):
+    // the 8-byte writes of 32 rows meet at most two to a bank, the row reads
+    // not at all.
+    char* os = Os[wave];
+#pragma unroll
+    for (int pair = 0; pair < NDB / 2; ++pair) {
+#pragma unroll
+      for (int dd = 0; dd < 2; ++dd) {
+        const f32x16 acc = block(2 * pair + dd);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 o4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[4 * g4 + r] * inv);
+          const int ch = (4 * dd + g4) ^ ((lr >> 1) & 7);
+          *reinterpret_cast<bf16x4*>(os + lr * 128 + ch * 16 + hh * 8) = o4;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 8 * i + (lane >> 3), pc = lane & 7;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(os + rr * 128 + ((pc ^ ((rr >> 1) & 7)) * 16));
+        const int orow = r_lo + 32 * g + rr;
+        if (orow < r_hi) *reinterpret_cast<u32x4*>(og + int64_t(orow) * rs + pair * 64 + pc * 8) = v;
+      }
+    }
+#else
     __bf16* dst = og + int64_t(row) * rs;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -428,6 +469,7 @@ __global__ __launch_bounds__(NW * 64) void lin_apply_kernel(const LinParams p) {
         }
       }
     }
+#endif
   }
 #endif
 }
@@ -513,7 +555,7 @@ __global__ __launch_bounds__(256) void fuse_kernel(const FuseParams p) {
 #endif
 
 #ifndef VDN_LIN_APPLY_NW
-#define VDN_LIN_APPLY_NW 8
+#define VDN_LIN_APPLY_NW 4
 #endif
 
 template <int D>

@@ -8,7 +8,7 @@ namespace vdn {
 
 // Rows of one linear-branch apply tile (a tile never spans two frame blocks).
 #ifndef VDN_LIN_ROW_TILE
-#define VDN_LIN_ROW_TILE 256
+#define VDN_LIN_ROW_TILE 512
 #endif
 constexpr int kLinRowTile = VDN_LIN_ROW_TILE;
 
