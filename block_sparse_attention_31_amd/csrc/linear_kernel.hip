@@ -14,8 +14,9 @@
 //   1. frame states: per (sample, head, non-anchor frame), S_f^T = V_f^T
 //      phi(K_f) on bf16 MFMA with K and V staged through LDS by DMA and read
 //      back transposed, plus z_f = sum phi(k), to an fp32 workspace;
-//   2. block states: per state element, the sum over each block's frames
-//      (fp32, in frame order), written as bf16 S_beta^T and fp32 z_beta;
+//   2. block states: per four state elements, the sum over each block's
+//      frames (fp32, in frame order), written as bf16 S_beta^T and fp32
+//      z_beta;
 //   3. apply: per (sample, head, row tile of one block), O^T = S_beta^T
 //      phi(Q)^T on bf16 MFMA with S_beta^T in LDS, the normaliser
 //      phi(q) . z_beta from the same products (z split into two bf16 rows).
@@ -301,7 +302,8 @@ __global__ __launch_bounds__(256) void lin_block_state_kernel(const LinParams p)
 // The LDS state has D rows of S^T plus a 32-row block whose rows 0 and 1
 // hold z in two bf16 parts (z_hi = bf16(z), z_lo = bf16(z - z_hi)) and the
 // rest zeros: its product gives the normaliser phi(q) . z with fp32
-// accumulation on the matrix cores, to about 2^-17 of z.
+// accumulation on the matrix cores, to about 2^-17 of z.  The output leaves
+// through a per-wave LDS tile so that stores write whole 128-byte lines.
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(const LinParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
