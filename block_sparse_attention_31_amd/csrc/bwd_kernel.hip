@@ -34,25 +34,30 @@ namespace vdn {
 
 namespace {
 
-// Per-row pass: one thread per (sample, token, head).
+// Per-row pass: D/8 lanes per (sample, token, head) row, 16 bytes of out and
+// dout each, so one load instruction covers whole rows; the dot product is
+// reduced across the row's lanes and its first lane writes the results.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rows_kernel(const BwdArgs a, int64_t total) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;  // ((b * S) + i) * H + h
-  if (idx >= total) return;
+  constexpr int LPR = D / 8;  // lanes per row (a power of two dividing 64)
+  const int64_t idx = (int64_t(blockIdx.x) * 256 + threadIdx.x) / LPR;  // ((b * S) + i) * H + h
+  const int c = int(threadIdx.x) % LPR;
+  const bool live = idx < total;
+  float acc = 0.f;
+  if (live) {
+    const bf16x8 x = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.out) + idx * D)[c];
+    const bf16x8 y = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.dout) + idx * D)[c];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(float(x[e]), float(y[e]), acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (!live || c != 0) return;
   const int h = int(idx % a.H);
   const int64_t bi = idx / a.H;
   const int i = int(bi % a.S);
   const int b = int(bi / a.S);
-  const bf16x8* o = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.out) + idx * D);
-  const bf16x8* g = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.dout) + idx * D);
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const bf16x8 x = o[c], y = g[c];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(float(x[e]), float(y[e]), acc);
-  }
   float sgv = 1.f;
   if (a.gate != nullptr) {
     sgv = 1.f / (1.f + __builtin_amdgcn_exp2f(-a.gate[idx] * kLog2e));
@@ -553,7 +558,10 @@ int launch_bwd(const BwdDqParams& dq, const BwdKvParams& kv, int head_dim, void*
   hipStream_t st = static_cast<hipStream_t>(stream);
   const BwdArgs& a = dq.a;
   const int64_t total = int64_t(a.B) * a.S * a.H;
-  const dim3 rgrid(unsigned((total + 255) / 256));
+  const int64_t rows_per_block = 256 / (head_dim / 8);
+  const int64_t row_blocks = (total + rows_per_block - 1) / rows_per_block;
+  if (row_blocks > INT32_MAX) return int(hipErrorInvalidConfiguration);
+  const dim3 rgrid(static_cast<unsigned>(row_blocks));
   const dim3 qgrid(unsigned(dq.per_xcd) * 8u), qblock(64 * kDqWaves);
   const dim3 kgrid(unsigned(kv.per_xcd) * 8u), kblock(64 * kKvWaves);
   if (head_dim == 128) {
