@@ -9,10 +9,12 @@
 //
 //   scores  S = sum_d q8 k8 (exact products, fp32 accumulation); the real
 //           score is S * s_q[h] * s_k[h] * scale, folded into one factor;
-//   weights P = 2^8 exp2(S c - m) with m the exact running maximum, so
-//           P <= 256 < 448 and weights down to 2^-17 of the row maximum stay
-//           above e4m3's smallest subnormal (2^-9); rounded to e4m3 with
-//           v_cvt_pk_fp8_f32 (round to nearest even).  The 2^8 cancels in
+//   weights P = 2^7 exp2(S c - m) with m a running maximum that lags the
+//           row's true maximum by at most 1 (the accumulator is rescaled
+//           only when the maximum grows by more), so P <= 2^8 < 448 and
+//           weights down to 2^-16..2^-17 of the row maximum stay above
+//           e4m3's smallest subnormal (2^-9); rounded to e4m3 with
+//           v_cvt_pk_fp8_f32 (round to nearest even).  The 2^7 cancels in
 //           O = acc / l and is taken out of the log-sum-exp;
 //   output  O = (P8 V8) * s_v[h] / l, where l = sum of the rounded P8, taken
 //           by one extra MFMA against an all-ones operand so that numerator
@@ -41,7 +43,14 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // e4m3fn encoding of 1.0 in every byte.
 [[maybe_unused]] constexpr int kFp8Ones = 0x38383838;
 // log2 of the factor applied to the weights before rounding them to e4m3.
-[[maybe_unused]] constexpr float kFp8PShift = 8.0f;
+// The running maximum may lag the true one by up to kFp8Slack (log2 units):
+// the accumulator is rescaled only when a row's maximum grows by more, and
+// P = 2^(8 - slack) exp2(S c - m) then still stays <= 2^8.
+#ifndef VDN_FP8_SLACK
+#define VDN_FP8_SLACK 1
+#endif
+[[maybe_unused]] constexpr float kFp8Slack = float(VDN_FP8_SLACK);
+[[maybe_unused]] constexpr float kFp8PShift = 8.0f - kFp8Slack;
 
 template <int D, int NW, int NS, int KT, int KPF>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) {
@@ -273,7 +282,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
 #pragma unroll
       for (int kb = 1; kb < NKB; ++kb) mx = fmaxf(mx, mb[kb]);
       mx = xhalf_max(mx) * c;
-      if (__any(mx > m_run)) {
+      if (__any(mx > m_run + kFp8Slack)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
