@@ -323,8 +323,8 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.dout = dout;
   a.gate = gate;
   a.lse = lse;
-  a.delta = workspace;
-  a.sg = workspace + size_t(batch) * size_t(heads) * size_t(g.S);
+  a.dw = workspace;
+  a.lw = workspace + size_t(batch) * size_t(heads) * size_t(g.S);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

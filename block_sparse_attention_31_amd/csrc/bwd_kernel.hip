@@ -14,9 +14,13 @@
 //   ds_ij   = p_ij (sg_i dp_ij - delta_i)
 //   dq_i    = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
 //   dv_j    = sum_i sg_i p_ij dout_i.
-// Three kernels: a per-row pass (delta, sg, dgate), dQ over query tiles with
-// the keys streaming through LDS (the forward's schedule), and dK/dV over key
-// tiles with the query rows streaming through LDS.
+// The gate folds into two per-row constants, lw_i = lse_i log2(e) - log2(sg_i)
+// and dw_i = delta_i / sg_i, so that sg_i p_ij = exp2(scale log2(e) q_i.k_j -
+// lw_i) and ds_ij = sg_i p_ij (dp_ij - dw_i): one exponential per pair yields
+// the dV weight directly.
+// Three kernels: a per-row pass (delta, dgate, lw, dw), dQ over query tiles
+// with the keys streaming through LDS (the forward's schedule), and dK/dV over
+// key tiles with the query rows streaming through LDS.
 //
 // Both tiled kernels read one LDS tile in two ways: as MFMA row operands
 // (ds_read_b128 of 16-byte chunks) and transposed (ds_read_b64_tr_b16).  The
@@ -64,8 +68,10 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const BwdArgs a, int64_t 
     a.dgate[idx] = acc * (1.f - sgv);
   }
   const int64_t r = (int64_t(b) * a.H + h) * a.S + i;
-  a.delta[r] = acc;
-  a.sg[r] = sgv;
+  // the gate folded into the row's constants: sg p = exp2(S c - lw) and
+  // ds = sg p (dp - dw); a gate that rounds to 0 gives lw = +inf (weights 0)
+  a.lw[r] = a.lse[r] * kLog2e - __log2f(sgv);
+  a.dw[r] = sgv > 0.f ? acc / sgv : 0.f;
 #endif
 }
 
@@ -73,13 +79,13 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(const BwdArgs a, int64_t 
 
 // ---------------------------------------------------------------------------
 // dQ: one workgroup = NW waves x 32 query rows of one (sample, head, query
-// block), keys in steps of KT through a 2-stage LDS ring (as the forward).
+// block), keys in steps of KT through an NS-stage LDS ring (as the forward).
 // Per step, in the transposed score layout (one query per lane):
 //   S^T  = K Q^T        (A = K rows from LDS, B = Q in registers)
 //   dP^T = V dO^T       (A = V rows from LDS, B = dO in registers)
-//   dS^T = P (sg dP - delta) scale, P = exp2(S c - lse log2 e)
+//   dS^T = W (dP - dw) scale, W = sg P = exp2(S c - lw)
 //   dQ^T += K^T dS^T    (A = K^T by transposing reads, B = dS^T packed to bf16)
-template <int D, int NW, int KT>
+template <int D, int NW, int KT, int NS>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int QW = 32;
@@ -93,14 +99,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
   constexpr int NDB = D / 32;
   constexpr int NKB = KT / 32;
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
+  static_assert(NS == 2 || NS == 3, "two or three stages");
   const BwdArgs& a = p.a;
 
+  // one array per stage (the third is a single byte when unused)
   __shared__ __attribute__((aligned(1024))) char Ks0[TILE];
   __shared__ __attribute__((aligned(1024))) char Ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) char Ks2[NS > 2 ? TILE : 1];
   __shared__ __attribute__((aligned(1024))) char Vs0[TILE];
   __shared__ __attribute__((aligned(1024))) char Vs1[TILE];
-  auto kstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Ks0 : Ks1; };
-  auto vstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Vs0 : Vs1; };
+  __shared__ __attribute__((aligned(1024))) char Vs2[NS > 2 ? TILE : 1];
+  auto kstage = [&](auto st) -> char* {
+    constexpr int i = decltype(st)::value;
+    return i == 0 ? Ks0 : i == 1 ? Ks1 : Ks2;
+  };
+  auto vstage = [&](auto st) -> char* {
+    constexpr int i = decltype(st)::value;
+    return i == 0 ? Vs0 : i == 1 ? Vs1 : Vs2;
+  };
 
   const int w = blockIdx.x;
   const int t = (w & 7) * p.per_xcd + (w >> 3);
@@ -142,14 +158,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
       oreg[ds] = row_ok ? *reinterpret_cast<const bf16x8*>(os + ds * 16) : bf16x8{};
     }
   }
-  // P = exp2(S c - L); rows past the tile get L = +inf (P = 0)
-  float L = __builtin_inff(), sgs = 0.f, dls = 0.f;
+  // sg P = exp2(S c - L) with L = lw; rows past the tile get L = +inf (P = 0)
+  float L = __builtin_inff(), dls = 0.f;
+  const float sgs = a.scale;
   if (row_ok) {
     const int64_t r = (int64_t(b) * a.H + h) * a.S + row0 + lrow;
-    L = a.lse[r] * kLog2e;
-    sgs = a.sg[r] * a.scale;
-    dls = a.delta[r] * a.scale;
+    L = a.lw[r];
+    dls = a.dw[r] * a.scale;
   }
+  // these loads complete before any DMA is issued: the compiler cannot count
+  // the DMA, and with loads of its own still pending at the loop it would
+  // wait on the DMA ring inside every step
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -218,10 +238,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
     }
   };
 
+  // per step: the K and V of step + NS - 1 are issued into the stage freed
+  // by the previous step, and the step's own stage is read
   auto body = [&](int step, auto st) {
     constexpr int s_ = decltype(st)::value;
-    issue(step + 1, kstage(IC<1 - s_>{}), kg);
-    issue(step + 1, vstage(IC<1 - s_>{}), vg);
+    issue(step + NS - 1, kstage(IC<(s_ + NS - 1) % NS>{}), kg);
+    issue(step + NS - 1, vstage(IC<(s_ + NS - 1) % NS>{}), vg);
     if (active) {
       const char* ks = kstage(st);
       f32x16 sc[NKB], dp[NKB];
@@ -255,20 +277,33 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, pk[kb][half], acc[db], 0, 0, 0);
           }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // the next step reads stage step + 1; the batches of steps step + 2 ..
+    // step + NS - 1 may still be in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
     lds_barrier();
   };
 
+  // prologue: steps 0 .. NS - 2 in flight (past the key list's end a step
+  // re-fetches its last key, so every step issues the same batch)
   issue(0, Ks0, kg);
   issue(0, Vs0, vg);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  if constexpr (NS > 2) {
+    issue(1, Ks1, kg);
+    issue(1, Vs1, vg);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));
   lds_barrier();
   for (int step = 0;;) {
     body(step, IC<0>{});
     if (++step >= nsteps) break;
-    body(step, IC<1>{});
+    body(step, IC<1 % NS>{});
     if (++step >= nsteps) break;
+    if constexpr (NS > 2) {
+      body(step, IC<2 % NS>{});
+      if (++step >= nsteps) break;
+    }
   }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA outlives the workgroup
 
   if (row_ok) {
     __bf16* dst = static_cast<__bf16*>(a.dq) + bh_off + int64_t(row0 + lrow) * rs;
@@ -292,8 +327,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
 // key per lane):
 //   S  = Q K^T      (A = Q rows from LDS, B = K in registers)
 //   dP = dO V^T     (A = dO rows from LDS, B = V rows from the LDS key tile)
-//   P = exp2(S c - lse log2 e), dS = P (sg dP - delta)
-//   dV^T += dO^T (sg P),  dK^T += Q^T dS  (A by transposing reads; B packed)
+//   W = sg P = exp2(S c - lw), dS = W (dP - dw)
+//   dV^T += dO^T W,  dK^T += Q^T dS  (A by transposing reads; B packed)
 // V of the workgroup's keys stays in LDS for the whole tile (read as B
 // operands), which keeps a wave within 256 registers: two waves per SIMD.
 template <int D, int NW, int QT>
@@ -311,7 +346,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
   constexpr int NQB = QT / 32;    // 32-row blocks per step
   constexpr int NVI = KW * RB / 1024;  // DMA instructions per wave for its V rows
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
-  static_assert(NW >= 3 && QT <= 64, "three waves stage the per-row constants, one row per lane");
+  static_assert(NW >= 2 && QT <= 64, "two waves stage the per-row constants, one row per lane");
   const BwdArgs& a = p.a;
 
   __shared__ __attribute__((aligned(1024))) char Qs0[TILE];
@@ -319,7 +354,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
   __shared__ __attribute__((aligned(1024))) char Os0[TILE];
   __shared__ __attribute__((aligned(1024))) char Os1[TILE];
   __shared__ __attribute__((aligned(1024))) char Vt[N * RB];   // V rows of the tile's keys
-  __shared__ __attribute__((aligned(16))) float Rs[2][3][QT];  // per stage: L, delta, sg
+  __shared__ __attribute__((aligned(16))) float Rs[2][2][QT];  // per stage: lw, dw
   auto qstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Qs0 : Qs1; };
   auto ostage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Os0 : Os1; };
 
@@ -420,20 +455,20 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
       }
     }
   };
-  // per-row constants of a step: waves 0, 1, 2 fetch L = lse log2 e, delta,
-  // sg for one row per lane (rows past the end: L = +inf, delta = sg = 0,
-  // which zeroes their weights)
+  // per-row constants of a step: waves 0 and 1 fetch lw and dw for one row
+  // per lane (rows past the end: lw = +inf, dw = 0, which zeroes their
+  // weights)
   // (the value is used, and so waited for, only when stored at the end of
   // the step: a wait right after the load would also drain the DMA)
-  const float* rsrc = (wave == 0 ? a.lse : wave == 1 ? a.delta : a.sg) + row_base;
+  const float* rsrc = (wave == 0 ? a.lw : a.dw) + row_base;
   auto fetch_rows = [&](int step) -> float {
     const int i = step * QT + lane;
-    if (wave > 2 || lane >= QT) return 0.f;
+    if (wave > 1 || lane >= QT) return 0.f;
     if (i >= n_rows) return wave == 0 ? __builtin_inff() : 0.f;
     return rsrc[vtoken(rl, i)];
   };
   auto store_rows = [&](int stage, float x) {
-    if (wave <= 2 && lane < QT) Rs[stage][wave][lane] = wave == 0 ? x * kLog2e : x;
+    if (wave <= 1 && lane < QT) Rs[stage][wave][lane] = x;
   };
 
   // row-operand offsets (row lr, logical chunk 2 ds + hh), for the streamed
@@ -484,16 +519,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
         const int row = qb * 32 + 8 * g4 + 4 * hh;
         const float4 Lr = *reinterpret_cast<const float4*>(&Rs[s_][0][row]);
         const float4 Dr = *reinterpret_cast<const float4*>(&Rs[s_][1][row]);
-        const float4 Gr = *reinterpret_cast<const float4*>(&Rs[s_][2][row]);
         const float Lv[4] = {Lr.x, Lr.y, Lr.z, Lr.w};
         const float Dv[4] = {Dr.x, Dr.y, Dr.z, Dr.w};
-        const float Gv[4] = {Gr.x, Gr.y, Gr.z, Gr.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * g4 + u;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -Lv[u]));
-          pg[r / 8][r % 8] = static_cast<__bf16>(pr * Gv[u]);
-          dsb[r / 8][r % 8] = static_cast<__bf16>(pr * __builtin_fmaf(Gv[u], dp[r], -Dv[u]));
+          const float w = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c, -Lv[u]));  // sg P
+          pg[r / 8][r % 8] = static_cast<__bf16>(w);
+          dsb[r / 8][r % 8] = static_cast<__bf16>(w * (dp[r] - Dv[u]));
         }
       }
       // dV^T += dO^T (sg P), dK^T += Q^T dS over the block's two 16-row halves
@@ -547,9 +580,20 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
 #endif
 }
 
+#ifndef VDN_KV_QT
+#define VDN_KV_QT 32
+#endif
+#ifndef VDN_DQ_KT
+#define VDN_DQ_KT 64
+#endif
+#ifndef VDN_DQ_NS
+#define VDN_DQ_NS 2
+#endif
 constexpr int kDqWaves = 8;
-constexpr int kDqKeys = 64;
+constexpr int kDqKeys = VDN_DQ_KT;
+constexpr int kDqStages = VDN_DQ_NS;
 constexpr int kKvWaves = 8;
+constexpr int kKvRows128 = VDN_KV_QT;  // query rows per dK/dV step at head_dim 128
 
 int bwd_dq_tile_m() { return 32 * kDqWaves; }
 int bwd_dkv_tile_n() { return 32 * kKvWaves; }
@@ -566,11 +610,11 @@ int launch_bwd(const BwdDqParams& dq, const BwdKvParams& kv, int head_dim, void*
   const dim3 kgrid(unsigned(kv.per_xcd) * 8u), kblock(64 * kKvWaves);
   if (head_dim == 128) {
     hipLaunchKernelGGL((bwd_rows_kernel<128>), rgrid, dim3(256), 0, st, a, total);
-    hipLaunchKernelGGL((bwd_dq_kernel<128, kDqWaves, kDqKeys>), qgrid, qblock, 0, st, dq);
-    hipLaunchKernelGGL((bwd_dkv_kernel<128, kKvWaves, 32>), kgrid, kblock, 0, st, kv);
+    hipLaunchKernelGGL((bwd_dq_kernel<128, kDqWaves, kDqKeys, kDqStages>), qgrid, qblock, 0, st, dq);
+    hipLaunchKernelGGL((bwd_dkv_kernel<128, kKvWaves, kKvRows128>), kgrid, kblock, 0, st, kv);
   } else if (head_dim == 64) {
     hipLaunchKernelGGL((bwd_rows_kernel<64>), rgrid, dim3(256), 0, st, a, total);
-    hipLaunchKernelGGL((bwd_dq_kernel<64, kDqWaves, kDqKeys>), qgrid, qblock, 0, st, dq);
+    hipLaunchKernelGGL((bwd_dq_kernel<64, kDqWaves, kDqKeys, kDqStages>), qgrid, qblock, 0, st, dq);
     hipLaunchKernelGGL((bwd_dkv_kernel<64, kKvWaves, 64>), kgrid, kblock, 0, st, kv);
   } else {
     return int(hipErrorInvalidValue);

@@ -147,6 +147,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
       }
     }
   }
+  // Q lands before any DMA is issued: the compiler cannot count the DMA, and
+  // with its own loads still pending at the loop it would wait on the whole
+  // ring inside every step
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   f32x16 acc[NDB];
   f32x16 lacc = f32x16{};  // every element: the row sum of the rounded weights

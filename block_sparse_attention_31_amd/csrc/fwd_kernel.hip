@@ -132,6 +132,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     for (int ds = 0; ds < NDS; ++ds)
       qreg[ds] = lrow < rows ? *reinterpret_cast<const bf16x8*>(src + ds * 16) : bf16x8{};
   }
+  // Q lands before any DMA is issued: the compiler cannot count the DMA, and
+  // with its own loads still pending at the loop it would wait on the whole
+  // ring inside every step
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   f32x16 acc[NDB];
   float m_run = -__builtin_inff(), l_run = 0.f;

@@ -63,8 +63,10 @@ struct BwdArgs {
   const void* dout;
   const float* gate;   // [B,S,H] or nullptr
   const float* lse;    // [B,H,S], natural log
-  float* delta;        // workspace [B,H,S]: sum_d dout * out
-  float* sg;           // workspace [B,H,S]: sigmoid(gate), 1 without a gate
+  float* dw;           // workspace [B,H,S]: (sum_d dout * out) / sg, 0 where sg is 0
+  float* lw;           // workspace [B,H,S]: lse log2(e) - log2(sg), so that
+                       // sg p_ij = exp2(scale log2(e) q_i.k_j - lw_i)
+                       // (sg = sigmoid(gate), 1 without a gate)
   void* dq;
   void* dk;
   void* dv;
