@@ -16,6 +16,29 @@
 
 namespace {
 
+// Tiles of each XCD's share (32 compute units) that run as two half-height
+// tiles at its end, from the share's size (measured on the 768p shape with
+// 1 to 32 heads): at most half a round in all, every tile (one round of
+// halves); a last round at most half full in one to four rounds, 16; else
+// none (a split then costs more than the idle end it fills).
+int split_tail_for(int per_xcd) {
+  if (per_xcd <= 16) return per_xcd;
+  if (per_xcd >= 32 && per_xcd < 128 && per_xcd % 32 <= 16) return 16;
+  return 0;
+}
+
+// Dispatch fields shared by the tiled kernels: each XCD's share of the tile
+// list, the half tiles at its end, and how many piles a (sample, head)'s
+// tiles are dealt into when it spans several shares.
+template <class P>
+void set_dispatch(P& p) {
+  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.split_tail = VDN_SPLIT_TAIL < 0 ? split_tail_for(p.per_xcd) : std::min(p.per_xcd, VDN_SPLIT_TAIL);
+  p.deal = (VDN_DEAL && p.per_xcd < p.tiles_per_bh)
+               ? std::min(8, (p.tiles_per_bh + p.per_xcd - 1) / p.per_xcd)
+               : 1;
+}
+
 thread_local std::string g_last_error;
 
 int fail(int code, const std::string& msg) {
@@ -249,7 +272,7 @@ int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float*
   p.n_qblocks = n;
   p.tiles_per_bh = prefix;
   p.total_tiles = prefix * batch * heads;
-  p.per_xcd = (p.total_tiles + 7) / 8;
+  set_dispatch(p);
 
   const int rc = vdn::launch_fwd(p, head_dim, dtype, hip_stream);
   if (rc != 0)
@@ -359,7 +382,7 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
   dq_p.n_blocks = n;
   dq_p.tiles_per_bh = prefix;
   dq_p.total_tiles = prefix * batch * heads;
-  dq_p.per_xcd = (dq_p.total_tiles + 7) / 8;
+  set_dispatch(dq_p);
 
   // dK/dV: key tiles, most query rows first
   const int tile_n = vdn::bwd_dkv_tile_n();
@@ -395,7 +418,7 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
   kv_p.n_blocks = n;
   kv_p.tiles_per_bh = prefix;
   kv_p.total_tiles = prefix * batch * heads;
-  kv_p.per_xcd = (kv_p.total_tiles + 7) / 8;
+  set_dispatch(kv_p);
 
   const int rc = vdn::launch_bwd(dq_p, kv_p, head_dim, hip_stream);
   if (rc != 0)

@@ -118,18 +118,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(const BwdDqParams p)
     return i == 0 ? Vs0 : i == 1 ? Vs1 : Vs2;
   };
 
-  const int w = blockIdx.x;
-  const int t = (w & 7) * p.per_xcd + (w >> 3);
+  const TileSlot slot = tile_slot(blockIdx.x, p.per_xcd, p.split_tail);
+  const int t = slot.tile;
   if (t >= p.total_tiles) return;
   const int bh = t / p.tiles_per_bh;
-  const int rank = t - bh * p.tiles_per_bh;
+  const int rank = undeal(t - bh * p.tiles_per_bh, p.tiles_per_bh, p.deal);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   int bi = 0;
   while (bi + 1 < p.n_blocks && p.blk[bi + 1].tile_prefix <= rank) ++bi;
   const KeyList kl = load_key_list(p.blk[bi]);
-  const int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
-  const int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
+  int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  if (slot.half != 0) {
+    const int off = (slot.half - 1) * (M / 2);
+    row0 += off;
+    rows = min(M / 2, rows - off);
+    if (rows <= 0) return;  // a tile of at most M/2 rows has no second half
+  }
   const int n_keys = kl.n_keys;
 
   const int tid = threadIdx.x;
@@ -358,11 +364,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
   auto qstage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Qs0 : Qs1; };
   auto ostage = [&](auto st) -> char* { return decltype(st)::value == 0 ? Os0 : Os1; };
 
-  const int w = blockIdx.x;
-  const int t = (w & 7) * p.per_xcd + (w >> 3);
+  const TileSlot slot = tile_slot(blockIdx.x, p.per_xcd, p.split_tail);
+  const int t = slot.tile;
   if (t >= p.total_tiles) return;
   const int bh = t / p.tiles_per_bh;
-  const int rank = t - bh * p.tiles_per_bh;
+  const int rank = undeal(t - bh * p.tiles_per_bh, p.tiles_per_bh, p.deal);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   int gi = 0;
@@ -382,7 +388,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
   rl.delta0 = __builtin_amdgcn_readfirstlane(kd.qiv_delta[0]);
   rl.delta1 = __builtin_amdgcn_readfirstlane(kd.qiv_delta[1]);
   rl.delta2 = 0;
-  const int key0 = (rank - kd.tile_prefix) * N;
+  // keys [key0, key_end) of the group belong to this tile (or half tile)
+  int key0 = (rank - kd.tile_prefix) * N;
+  int key_end = min(kl.n_keys, key0 + N);
+  if (slot.half != 0) {
+    key0 += (slot.half - 1) * (N / 2);
+    key_end = min(key_end, key0 + N / 2);
+    if (key0 >= key_end) return;  // a tile of at most N/2 keys has no second half
+  }
   const int n_rows = rl.n_keys;
 
   const int tid = threadIdx.x;
@@ -401,7 +414,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
 
   // this lane's key (B-operand column lr): K row in registers
   const int kj = key0 + wave * KW + lr;
-  const bool key_ok = kj < kl.n_keys;
+  const bool key_ok = kj < key_end;
+  // a wave whose keys all lie past the tile only helps with the DMA and the
+  // barriers
+  const bool active = key0 + wave * KW < key_end;
   const int ktok = vtoken(kl, min(kj, kl.n_keys - 1));
   bf16x8 kreg[NDS];
   {
@@ -498,6 +514,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dkv_kernel(const BwdKvParams p
     const char* osb = ostage(st);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
+      if (!active) break;
       const char* qs = qsb + qb * 32 * RB;
       const char* os = osb + qb * 32 * RB;
       f32x16 sc = f32x16{}, dp = f32x16{};
@@ -606,8 +623,8 @@ int launch_bwd(const BwdDqParams& dq, const BwdKvParams& kv, int head_dim, void*
   const int64_t row_blocks = (total + rows_per_block - 1) / rows_per_block;
   if (row_blocks > INT32_MAX) return int(hipErrorInvalidConfiguration);
   const dim3 rgrid(static_cast<unsigned>(row_blocks));
-  const dim3 qgrid(unsigned(dq.per_xcd) * 8u), qblock(64 * kDqWaves);
-  const dim3 kgrid(unsigned(kv.per_xcd) * 8u), kblock(64 * kKvWaves);
+  const dim3 qgrid(unsigned(dq.per_xcd + dq.split_tail) * 8u), qblock(64 * kDqWaves);
+  const dim3 kgrid(unsigned(kv.per_xcd + kv.split_tail) * 8u), kblock(64 * kKvWaves);
   if (head_dim == 128) {
     hipLaunchKernelGGL((bwd_rows_kernel<128>), rgrid, dim3(256), 0, st, a, total);
     hipLaunchKernelGGL((bwd_dq_kernel<128, kDqWaves, kDqKeys, kDqStages>), qgrid, qblock, 0, st, dq);

@@ -88,6 +88,44 @@ __device__ __forceinline__ int interval_delta(const KeyList& k, int j) {
 template <int N>
 using IC = std::integral_constant<int, N>;
 
+// Workgroup slot -> query tile.  Workgroups are dealt round-robin over the 8
+// XCDs, and XCD x takes the tiles [x per_xcd, (x + 1) per_xcd) of the tile
+// list in order, so consecutive tiles of one (sample, head) share an L2.  The
+// last `split` tiles of each XCD's share run as two half tiles each (slots
+// per_xcd - split .. per_xcd + split - 1): dispatched last, the shorter work
+// evens out when the XCD's compute units finish.  `half` is 0 for a whole
+// tile, 1 or 2 for its first or second half.
+struct TileSlot {
+  int tile, half;
+};
+// A (sample, head)'s tiles, sorted longest first, are dealt into `k` piles
+// (tile s to pile s mod k) when the head spans k XCDs' shares, so that each
+// share gets an even mix of long and short tiles; position r in the dealt
+// order -> position in the sorted order.
+__device__ __forceinline__ int undeal(int r, int n, int k) {
+  if (k <= 1) return r;
+  const int q = (n + k - 1) / k;       // entries of the first piles
+  const int full = n % k == 0 ? k : n % k;  // piles holding q entries
+  int pile, i;
+  if (r < full * q) {
+    pile = r / q;
+    i = r - pile * q;
+  } else {
+    const int r2 = r - full * q;
+    pile = full + r2 / (q - 1);
+    i = r2 - (pile - full) * (q - 1);
+  }
+  return i * k + pile;
+}
+
+__device__ __forceinline__ TileSlot tile_slot(int w, int per_xcd, int split) {
+  const int x = w & 7, u = w >> 3;
+  const int whole = per_xcd - split;
+  if (u < whole) return {x * per_xcd + u, 0};
+  const int hs = u - whole;
+  return {x * per_xcd + whole + (hs >> 1), 1 + (hs & 1)};
+}
+
 // Sets the scores of keys past the end of the key list to -inf on a partial
 // last step.  Score register (kb, r) of a 32x32 MFMA result holds key
 // 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 of the step; `lim` (wave-uniform)

@@ -97,19 +97,25 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
     return st == 0 ? Vs0 : st == 1 ? Vs1 : st == 2 ? Vs2 : Vs3;
   };
 
-  // ---- which tile (XCD-aware remap, as in the bf16 kernel)
-  const int w = blockIdx.x;
-  const int t = (w & 7) * p.per_xcd + (w >> 3);
+  // ---- which tile (XCD-aware, the last tiles of each XCD in halves)
+  const TileSlot slot = tile_slot(blockIdx.x, p.per_xcd, p.split_tail);
+  const int t = slot.tile;
   if (t >= p.total_tiles) return;
   const int bh = t / p.tiles_per_bh;
-  const int rank = t - bh * p.tiles_per_bh;
+  const int rank = undeal(t - bh * p.tiles_per_bh, p.tiles_per_bh, p.deal);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   int bi = 0;
   while (bi + 1 < p.n_qblocks && p.blk[bi + 1].tile_prefix <= rank) ++bi;
   const KeyList kl = load_key_list(p.blk[bi]);
-  const int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
-  const int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
+  int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  if (slot.half != 0) {
+    const int off = (slot.half - 1) * (M / 2);
+    row0 += off;
+    rows = min(M / 2, rows - off);
+    if (rows <= 0) return;  // a tile of at most M/2 rows has no second half
+  }
   const int n_keys = kl.n_keys;
 
   const int tid = threadIdx.x;
@@ -412,7 +418,7 @@ int launch_fwd_fp8(const FwdParams& p, int head_dim, void* stream) {
   constexpr int kStages = VDN_FP8_STAGES;
   constexpr int kKeysPerStep = VDN_FP8_KT;
   constexpr int kReadAhead = VDN_FP8_KPF;
-  const dim3 grid(unsigned(p.per_xcd) * 8u);
+  const dim3 grid(unsigned(p.per_xcd + p.split_tail) * 8u);
   const dim3 block(64 * kWaves);
   if (head_dim != 128) return int(hipErrorInvalidValue);
   hipLaunchKernelGGL((fwd_fp8_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead>), grid, block, 0, static_cast<hipStream_t>(stream), p);

@@ -90,14 +90,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     return st == 0 ? Vs0 : st == 1 ? Vs1 : st == 2 ? Vs2 : Vs3;
   };
 
-  // ---- which tile: XCD-aware remap so that consecutive tiles of one
-  // (sample, head) land on the same XCD (workgroups are dealt round-robin
-  // over the 8 XCDs).
-  const int w = blockIdx.x;
-  const int t = (w & 7) * p.per_xcd + (w >> 3);
+  // ---- which tile (XCD-aware, the last tiles of each XCD in halves)
+  const TileSlot slot = tile_slot(blockIdx.x, p.per_xcd, p.split_tail);
+  const int t = slot.tile;
   if (t >= p.total_tiles) return;
   const int bh = t / p.tiles_per_bh;
-  const int rank = t - bh * p.tiles_per_bh;
+  const int rank = undeal(t - bh * p.tiles_per_bh, p.tiles_per_bh, p.deal);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   int bi = 0;
@@ -106,8 +104,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // the kernel-argument table with a runtime index inside the loop would be a
   // vector-memory load, and its wait would also drain the DMA in flight).
   const KeyList kl = load_key_list(p.blk[bi]);
-  const int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
-  const int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  int row0 = p.blk[bi].row_lo + (rank - p.blk[bi].tile_prefix) * M;
+  int rows = min(M, p.blk[bi].row_lo + p.blk[bi].rows - row0);
+  if (slot.half != 0) {
+    const int off = (slot.half - 1) * (M / 2);
+    row0 += off;
+    rows = min(M / 2, rows - off);
+    if (rows <= 0) return;  // a tile of at most M/2 rows has no second half
+  }
   const int n_keys = kl.n_keys;
 
   const int tid = threadIdx.x;
@@ -432,7 +436,7 @@ int kernel_tile_m(int head_dim, int dtype) {
 }
 
 int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
-  const dim3 grid(unsigned(p.per_xcd) * 8u);
+  const dim3 grid(unsigned(p.per_xcd + p.split_tail) * 8u);
   const dim3 block(64 * kWaves);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == 1) return launch_fwd_fp8(p, head_dim, stream);

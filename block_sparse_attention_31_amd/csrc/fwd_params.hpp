@@ -20,6 +20,16 @@ struct QBlockDesc {
   int32_t iv_delta[3];  // token = virtual index + delta
 };
 
+// Trailing tiles of each XCD's share of the tile list that run as two
+// half-height tiles: -1 picks the count from the number of tiles, n >= 0
+// fixes it (0 turns the split off).
+#ifndef VDN_SPLIT_TAIL
+#define VDN_SPLIT_TAIL -1
+#endif
+#ifndef VDN_DEAL
+#define VDN_DEAL 1
+#endif
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -34,6 +44,8 @@ struct FwdParams {
   int32_t tiles_per_bh;    // query tiles per (sample, head)
   int32_t total_tiles;     // tiles_per_bh * B * H
   int32_t per_xcd;         // ceil(total_tiles / 8)
+  int32_t split_tail;      // trailing tiles of each XCD's share run as two halves
+  int32_t deal;            // piles each (sample, head)'s tile list is dealt into
   QBlockDesc blk[kMaxQueryBlocks];
 };
 
@@ -79,12 +91,14 @@ struct BwdArgs {
 struct BwdDqParams {
   BwdArgs a;
   int32_t n_blocks, tiles_per_bh, total_tiles, per_xcd;
+  int32_t split_tail, deal;  // as in FwdParams
   QBlockDesc blk[kMaxQueryBlocks];  // query blocks in launch order
 };
 
 struct BwdKvParams {
   BwdArgs a;
   int32_t n_blocks, tiles_per_bh, total_tiles, per_xcd;
+  int32_t split_tail, deal;  // as in FwdParams
   KBlockDesc blk[kMaxQueryBlocks];  // key groups in launch order
 };
 

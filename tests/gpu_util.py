@@ -13,6 +13,11 @@ from block_sparse_attention_31_amd import synth
 BF16_MAX_ABS = 2e-2
 FP8_MAX_ABS = 6e-2
 BF16_REL_L2 = 1e-2
+# Each weight is rounded to bf16 (relative error <= 2^-9) before the row sum,
+# so the log-sum-exp is off by at most ln(1 + 2^-9) (+ fp32 rounding).  The
+# default 1e-3 bar holds for N(0,1) inputs, whose weights spread over many
+# keys; rows sharpened by outlier channels can reach the bound itself.
+BF16_LSE_BOUND = float(np.log1p(2.0 ** -9)) + 1e-5
 
 
 def gpu_available() -> bool:

@@ -15,7 +15,7 @@ import oracle
 from block_sparse_attention_31_amd import binding as B
 from block_sparse_attention_31_amd import synth
 
-from .gpu_util import (FP8_MAX_ABS, compare, gpu_available, oracle_inputs, run_gpu, sample_rows,
+from .gpu_util import (BF16_LSE_BOUND, FP8_MAX_ABS, compare, gpu_available, oracle_inputs, run_gpu, sample_rows,
                        subset_heads, value_channel_rms)
 
 pytestmark = [pytest.mark.gpu,
@@ -91,6 +91,23 @@ def test_workload_sampled(name):
     _log(name, compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows))
     # every output element is finite
     assert np.isfinite(og).all()
+
+
+def test_medium_four_heads_dealt_full():
+    """Four heads of the medium shape: 33 tiles per XCD share, so each head's
+    tile list is dealt over two shares and the last 16 tiles of every share
+    run as two 128-row halves.  Every row of two heads against the oracle."""
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["medium"], name="medium-h4", H=4)
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w)
+    heads = [1, 2]
+    sub = subset_heads(inp, heads)
+    orf, lrf = oracle.attend(*oracle_inputs(sub), w.F, w.T, w.N, w.Bf)
+    # 2% outlier channels (x8): max-abs in units of each value channel's RMS,
+    # lse within the bf16 rounding bound of the row sum
+    _log("medium-h4", compare(og[:, :, heads], lg[:, heads], orf, lrf,
+                              v_rms=value_channel_rms(sub), lse_tol=BF16_LSE_BOUND))
 
 
 def test_768p_dense_mode_sampled():

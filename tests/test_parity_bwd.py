@@ -132,6 +132,24 @@ def test_medium_two_heads_full():
     check("medium heads 0,11", [None if g is None else g[:, :, heads] for g in got], ref)
 
 
+def test_medium_four_heads_dealt_full():
+    # four heads of the medium shape: each head's dQ and dK/dV tiles are dealt
+    # over two XCD shares and the last 16 tiles of every share run as halves;
+    # all gradients of two heads compared element by element
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["medium"], name="medium-h4", H=4)
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    got = run_bwd(inp, dout, w)
+    heads = [0, 3]
+    idx = torch.tensor(heads)
+    sub = {n: inp[n].index_select(2, idx).contiguous() for n in ("q", "k", "v")}
+    sub["gate"] = inp["gate"].index_select(2, idx).contiguous()
+    sub["scales"] = None
+    ref = _oracle(sub, dout.index_select(2, idx).contiguous(), w)
+    check("medium-h4 heads 0,3", [None if g is None else g[:, :, heads] for g in got], ref)
+
+
 def test_long_video_sampled():
     # two samples with their own seeds, 42 frames (nine blocks, the last of
     # two frames): dq and dgate of sampled rows of two heads, every gradient
