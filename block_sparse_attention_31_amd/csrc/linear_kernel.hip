@@ -404,7 +404,6 @@ __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(
   bf16x8 qn[NDS];
   if (wave < ngroups) load_q(wave, qn);
   for (int g = wave; g < ngroups; g += NW) {
-    const int row = r_lo + 32 * g + lr;
     bf16x8 bq[NDS];
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) bq[ds] = qn[ds];
