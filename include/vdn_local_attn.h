@@ -241,11 +241,16 @@ int vdn_local_attn_count_pairs(int F, int tokens_per_frame, int n_text,
                                int64_t* anchor_added);
 
 /*
- * Host only.  The per-(sample, head) query-tile work list in launch order
- * (longest key list first; ties by block index, then row): entries
- * [capacity][4] int32 = {query block, first row, rows, keys}, tiles of
- * `tile_m` rows that never straddle a block boundary.  *n_entries receives
- * the count; VDN_ERR_CAPACITY if capacity is too small.
+ * Host only.  The per-(sample, head) query-tile work list (longest key list
+ * first; ties by block index, then row): entries [capacity][4] int32 =
+ * {query block, first row, rows, keys}, tiles of `tile_m` rows that never
+ * straddle a block boundary.  *n_entries receives the count;
+ * VDN_ERR_CAPACITY if capacity is too small.  The kernels concatenate these
+ * lists over (sample, head) and give each of the 8 XCDs one contiguous
+ * eighth, in order; a list that spans several eighths is dealt over them
+ * (entry s to the (s mod k)-th), and the last tiles of an eighth may run as
+ * two halves of tile_m / 2 rows (schedule only: the results do not depend
+ * on it).
  */
 int vdn_local_attn_tile_schedule(int F, int tokens_per_frame, int n_text,
                                  int block_frames, int tile_m, int32_t* out,
