@@ -36,9 +36,10 @@
 #ifndef VDN_LIN_APPLY_STAGE
 #define VDN_LIN_APPLY_STAGE 1
 #endif
-// waves per SIMD the apply kernel is compiled for (4: two workgroups per CU)
+// waves per SIMD the apply kernel is compiled for: 2, the two 4-wave
+// workgroups per CU that its LDS allows (one wave per SIMD each)
 #ifndef VDN_LIN_APPLY_MINW
-#define VDN_LIN_APPLY_MINW 4
+#define VDN_LIN_APPLY_MINW 2
 #endif
 
 namespace vdn {
