@@ -1,6 +1,7 @@
 """MI355X-native local-window attention: the local Softmax branch of VDN-H3
 hybrid video attention (forward and backward), the complement linear branch
-and the two-branch fusion, as hand-written HIP for gfx950 behind a C ABI.
+and the two-branch fusion (separately, or in the softmax branch's epilogue),
+as hand-written HIP for gfx950 behind a C ABI.
 
 The HIP library is loaded lazily on the first call (see binding.lib()); there
 is no CPU fallback.
@@ -11,10 +12,13 @@ from .binding import (  # noqa: F401
     VDN_FP8_E4M3,
     VdnError,
     lib,
+    hybrid_attn_fwd,
     hybrid_fuse,
     linear_branch_fwd,
     local_attn_bwd,
     local_attn_fwd,
+    vdn_hybrid_attn_fwd,
+    vdn_hybrid_attn_workspace_bytes,
     vdn_hybrid_fuse,
     vdn_last_error,
     vdn_linear_branch_fwd,

@@ -45,6 +45,8 @@ SIGNATURES = {
     "vdn_linear_branch_fwd": (_i, [_p] * 4 + [_i] * 7 + [_p, _i64, _p]),
     "vdn_linear_branch_workspace_bytes": (_i64, [_i] * 7),
     "vdn_hybrid_fuse": (_i, [_p, _p, _p, _p, _f, _p, _i64, _i, _i, _p]),
+    "vdn_hybrid_attn_fwd": (_i, [_p] * 6 + [_f, _p] + [_i] * 7 + [_f, _p, _p, _i64, _p]),
+    "vdn_hybrid_attn_workspace_bytes": (_i64, [_i] * 7),
     "vdn_last_error": (ctypes.c_char_p, []),
 }
 
@@ -355,4 +357,64 @@ def hybrid_fuse(soft_out, lin_out, gate_lin, norm_weight, eps: float = 1e-6):
     import torch
     out = torch.empty_like(soft_out)
     vdn_hybrid_fuse(soft_out, lin_out, gate_lin, norm_weight, out, eps)
+    return out
+
+
+def vdn_hybrid_attn_workspace_bytes(F: int, tokens_per_frame: int, n_text: int, block_frames: int,
+                                    heads: int, head_dim: int, batch: int) -> int:
+    return _check(lib().vdn_hybrid_attn_workspace_bytes(F, tokens_per_frame, n_text, block_frames,
+                                                        heads, head_dim, batch))
+
+
+def vdn_hybrid_attn_fwd(q, k, v, gate, gate_lin, norm_weight, out, F: int, tokens_per_frame: int,
+                        n_text: int, block_frames: int = 5, eps: float = 1e-6,
+                        softmax_scale: float = 0.0, lse=None, workspace=None, stream=None) -> None:
+    """Enqueue the hybrid attention output (linear branch, then the softmax
+    branch with the fusion in its epilogue) on `stream`.
+
+    q, k, v, out: [B, S, H, D] bf16 CUDA tensors; gate (or None) and gate_lin
+    [B, S, H] fp32; norm_weight [H, D] (or H*D) fp32; lse [B, H, S] fp32 or
+    None; workspace: a contiguous GPU tensor of at least
+    vdn_hybrid_attn_workspace_bytes bytes."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    B, S, H, D = q.shape
+    for name, t, shape in (("gate", gate, (B, S, H)), ("gate_lin", gate_lin, (B, S, H)),
+                           ("norm_weight", norm_weight, None), ("lse", lse, (B, H, S))):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a contiguous fp32 GPU tensor")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if gate_lin is None or norm_weight is None:
+        raise ValueError("gate_lin and norm_weight are required")
+    if norm_weight.numel() != H * D:
+        raise ValueError(f"norm_weight must hold {H * D} values, got {norm_weight.numel()}")
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().vdn_hybrid_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gate_lin), _ptr(norm_weight), float(eps),
+        _ptr(out), F, tokens_per_frame, n_text, block_frames, H, D, B, float(softmax_scale),
+        _ptr(lse), _ptr(workspace), nbytes, ctypes.c_void_p(stream))
+    _check(rc)
+
+
+def hybrid_attn_fwd(q, k, v, gate, gate_lin, norm_weight, *, F: int, tokens_per_frame: int,
+                    n_text: int, block_frames: int = 5, eps: float = 1e-6, softmax_scale: float = 0.0):
+    """Allocating convenience wrapper: returns the hybrid attention output."""
+    import torch
+    B, S, H, D = q.shape
+    out = torch.empty_like(q)
+    nbytes = vdn_hybrid_attn_workspace_bytes(F, tokens_per_frame, n_text, block_frames, H, D, B)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    vdn_hybrid_attn_fwd(q, k, v, gate, gate_lin, norm_weight, out, F, tokens_per_frame, n_text,
+                        block_frames, eps=eps, softmax_scale=softmax_scale, workspace=ws)
     return out

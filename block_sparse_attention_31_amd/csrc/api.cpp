@@ -59,6 +59,18 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 bool aligned(const void* ptr, uintptr_t n) { return (reinterpret_cast<uintptr_t>(ptr) % n) == 0; }
 
+// The linear branch's share of vdn_hybrid_attn_fwd, passed to the softmax
+// branch's epilogue.
+struct FuseArgs {
+  const void* lin;
+  const float* ss;
+  const float* gate_lin;
+  const float* weight;
+  float eps;
+};
+
+uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
 }  // namespace
 
 extern "C" {
@@ -178,10 +190,11 @@ int vdn_local_attn_kernel_tile_m(int head_dim, int dtype) {
   return vdn::kernel_tile_m(head_dim, dtype);
 }
 
-int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float* gate, void* out,
-                       int F, int tokens_per_frame, int n_text, int block_frames, int heads,
-                       int head_dim, int dtype, int batch, const float* qkv_scales,
-                       float softmax_scale, float* lse, void* hip_stream) {
+static int local_attn_fwd_impl(const void* q, const void* k, const void* v, const float* gate,
+                               void* out, int F, int tokens_per_frame, int n_text, int block_frames,
+                               int heads, int head_dim, int dtype, int batch,
+                               const float* qkv_scales, float softmax_scale, float* lse,
+                               void* hip_stream, const FuseArgs* fuse) {
   vdn::Geometry g;
   std::string err;
   if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
@@ -273,11 +286,27 @@ int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float*
   p.tiles_per_bh = prefix;
   p.total_tiles = prefix * batch * heads;
   set_dispatch(p);
+  if (fuse != nullptr) {
+    p.lin = fuse->lin;
+    p.lin_ss = fuse->ss;
+    p.gate_lin = fuse->gate_lin;
+    p.lin_w = fuse->weight;
+    p.lin_eps = fuse->eps;
+  }
 
   const int rc = vdn::launch_fwd(p, head_dim, dtype, hip_stream);
   if (rc != 0)
     return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
   return ok();
+}
+
+int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float* gate, void* out,
+                       int F, int tokens_per_frame, int n_text, int block_frames, int heads,
+                       int head_dim, int dtype, int batch, const float* qkv_scales,
+                       float softmax_scale, float* lse, void* hip_stream) {
+  return local_attn_fwd_impl(q, k, v, gate, out, F, tokens_per_frame, n_text, block_frames, heads,
+                             head_dim, dtype, batch, qkv_scales, softmax_scale, lse, hip_stream,
+                             nullptr);
 }
 
 int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float* gate,
@@ -440,10 +469,10 @@ int64_t vdn_linear_branch_workspace_bytes(int F, int tokens_per_frame, int n_tex
   return int64_t(vdn::linear_workspace(batch, heads, g.F, g.nb, head_dim).total);
 }
 
-int vdn_linear_branch_fwd(const void* q, const void* k, const void* v, void* out, int F,
-                          int tokens_per_frame, int n_text, int block_frames, int heads,
-                          int head_dim, int batch, void* workspace, int64_t workspace_bytes,
-                          void* hip_stream) {
+static int linear_branch_fwd_impl(const void* q, const void* k, const void* v, void* out, int F,
+                                  int tokens_per_frame, int n_text, int block_frames, int heads,
+                                  int head_dim, int batch, void* workspace,
+                                  int64_t workspace_bytes, void* hip_stream, float* row_ss) {
   const int64_t need = vdn_linear_branch_workspace_bytes(F, tokens_per_frame, n_text, block_frames,
                                                          heads, head_dim, batch);
   if (need < 0) return int(need);
@@ -503,11 +532,88 @@ int vdn_linear_branch_fwd(const void* q, const void* k, const void* v, void* out
   if (total > INT32_MAX / 2) return fail(VDN_ERR_OVERFLOW, "too many row tiles");
   p.tiles_per_bh = int32_t(per_bh);
   p.total_tiles = int32_t(total);
+  p.ss = row_ss;
 
   const int rc = vdn::launch_linear(p, head_dim, hip_stream);
   if (rc != 0)
     return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
   return ok();
+}
+
+int vdn_linear_branch_fwd(const void* q, const void* k, const void* v, void* out, int F,
+                          int tokens_per_frame, int n_text, int block_frames, int heads,
+                          int head_dim, int batch, void* workspace, int64_t workspace_bytes,
+                          void* hip_stream) {
+  return linear_branch_fwd_impl(q, k, v, out, F, tokens_per_frame, n_text, block_frames, heads,
+                                head_dim, batch, workspace, workspace_bytes, hip_stream, nullptr);
+}
+
+int64_t vdn_hybrid_attn_workspace_bytes(int F, int tokens_per_frame, int n_text, int block_frames,
+                                        int heads, int head_dim, int batch) {
+  const int64_t lin = vdn_linear_branch_workspace_bytes(F, tokens_per_frame, n_text, block_frames,
+                                                        heads, head_dim, batch);
+  if (lin < 0) return lin;
+  vdn::Geometry g;
+  std::string err;
+  vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err);
+  const uint64_t rows = uint64_t(batch) * uint64_t(g.S) * uint64_t(heads);
+  if (rows > (uint64_t(1) << 40) / uint64_t(head_dim)) return fail(VDN_ERR_OVERFLOW, "tensor element count overflows");
+  ok();
+  return int64_t(up256(uint64_t(lin)) + up256(rows * uint64_t(head_dim) * 2u) + up256(rows * 4u));
+}
+
+int vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const float* gate,
+                        const float* gate_lin, const float* norm_weight, float eps, void* out,
+                        int F, int tokens_per_frame, int n_text, int block_frames, int heads,
+                        int head_dim, int batch, float softmax_scale, float* lse, void* workspace,
+                        int64_t workspace_bytes, void* hip_stream) {
+  const int64_t need = vdn_hybrid_attn_workspace_bytes(F, tokens_per_frame, n_text, block_frames,
+                                                       heads, head_dim, batch);
+  if (need < 0) return int(need);
+  const int64_t lin_need = vdn_linear_branch_workspace_bytes(F, tokens_per_frame, n_text,
+                                                             block_frames, heads, head_dim, batch);
+  vdn::Geometry g;
+  std::string err;
+  vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err);
+  if (gate_lin == nullptr || norm_weight == nullptr || workspace == nullptr)
+    return fail(VDN_ERR_INVALID_ARG, "gate_lin, norm_weight and workspace must be non-NULL");
+  if (!std::isfinite(eps) || eps < 0.f) return fail(VDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (workspace_bytes < need)
+    return fail(VDN_ERR_INVALID_ARG, "workspace of " + std::to_string(workspace_bytes) + " bytes, " +
+                                         std::to_string(need) + " needed");
+  if (!aligned(workspace, 256)) return fail(VDN_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (!aligned(norm_weight, 16)) return fail(VDN_ERR_ALIGNMENT, "norm_weight must be 16-byte aligned");
+  if (!aligned(gate_lin, 4)) return fail(VDN_ERR_ALIGNMENT, "gate_lin must be 4-byte aligned");
+  const uint64_t rows = uint64_t(batch) * uint64_t(g.S) * uint64_t(heads);
+  const size_t t_bytes = size_t(rows) * size_t(head_dim) * 2u;
+  const size_t g_bytes = size_t(rows) * 4u;
+  const size_t w_bytes = size_t(heads) * size_t(head_dim) * 4u;
+  const size_t l_bytes = size_t(rows) * 4u;
+  struct Span {
+    const void* p;
+    size_t n;
+  };
+  const Span others[] = {{q, t_bytes}, {k, t_bytes}, {v, t_bytes}, {out, t_bytes}, {gate, g_bytes},
+                         {gate_lin, g_bytes}, {norm_weight, w_bytes}, {lse, l_bytes}};
+  for (const Span& x : others)
+    if (x.p != nullptr && overlaps(workspace, size_t(need), x.p, x.n))
+      return fail(VDN_ERR_INVALID_ARG, "the workspace overlaps an input or output");
+  const Span fuse_in[] = {{gate_lin, g_bytes}, {norm_weight, w_bytes}};
+  for (const Span& x : fuse_in)
+    if (overlaps(out, t_bytes, x.p, x.n) || (lse != nullptr && overlaps(lse, l_bytes, x.p, x.n)))
+      return fail(VDN_ERR_INVALID_ARG, "out or lse overlaps gate_lin or norm_weight");
+
+  // workspace: the linear branch's own, then its output, then the per
+  // (token, head) sums of squares of that output
+  char* ws = static_cast<char*>(workspace);
+  void* lin_out = ws + up256(uint64_t(lin_need));
+  float* row_ss = reinterpret_cast<float*>(ws + up256(uint64_t(lin_need)) + up256(uint64_t(t_bytes)));
+  int rc = linear_branch_fwd_impl(q, k, v, lin_out, F, tokens_per_frame, n_text, block_frames, heads,
+                                  head_dim, batch, ws, lin_need, hip_stream, row_ss);
+  if (rc != 0) return rc;
+  const FuseArgs fuse{lin_out, row_ss, gate_lin, norm_weight, eps};
+  return local_attn_fwd_impl(q, k, v, gate, out, F, tokens_per_frame, n_text, block_frames, heads,
+                             head_dim, VDN_BF16, batch, nullptr, softmax_scale, lse, hip_stream, &fuse);
 }
 
 int vdn_hybrid_fuse(const void* soft_out, const void* lin_out, const float* gate_lin,

@@ -136,6 +136,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     for (int ds = 0; ds < NDS; ++ds)
       qreg[ds] = lrow < rows ? *reinterpret_cast<const bf16x8*>(src + ds * 16) : bf16x8{};
   }
+  // With the two-branch fusion: the row's linear-branch factor, sigmoid of
+  // its gate over the token's RMS (from the per-head sums of squares), read
+  // here so that its loads overlap Q's.
+  float lin_coef = 0.f;
+  if (p.lin != nullptr) {
+    const int lrow = wave * QW + lr;
+    if (lrow < rows) {
+      const int64_t tok = int64_t(b) * p.S + row0 + lrow;
+      const float* ssr = p.lin_ss + tok * p.H;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int i = 0; i < p.H; ++i) s4[i & 3] += ssr[i];
+      const float gl = 1.f / (1.f + __builtin_amdgcn_exp2f(-p.gate_lin[tok * p.H + h] * kLog2e));
+      lin_coef = gl / __builtin_sqrtf((s4[0] + s4[1] + s4[2] + s4[3]) / float(p.H * D) + p.lin_eps);
+    }
+  }
   // Q lands before any DMA is issued: the compiler cannot count the DMA, and
   // with its own loads still pending at the loop it would wait on the whole
   // ring inside every step
@@ -389,14 +405,38 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       scale *= 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
     }
     __bf16* dst = og + int64_t(row) * rs;
+    if (p.lin == nullptr) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+      for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 o4;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 o4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[db][g4 * 4 + r] * scale);
-        *reinterpret_cast<bf16x4*>(dst + db * 32 + g4 * 8 + hh * 4) = o4;
+          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[db][g4 * 4 + r] * scale);
+          *reinterpret_cast<bf16x4*>(dst + db * 32 + g4 * 8 + hh * 4) = o4;
+        }
+      }
+    } else {
+      // the two branches summed before the one rounding: the token's
+      // linear-branch row, scaled by its factor and the norm weight, joins
+      // this row
+      const float coef = lin_coef;
+      const __bf16* lsrc = static_cast<const __bf16*>(p.lin) + bh_off + int64_t(row) * rs;
+      const float* wsrc = p.lin_w + h * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = db * 32 + g4 * 8 + hh * 4;
+          const bf16x4 l4 = *reinterpret_cast<const bf16x4*>(lsrc + col);
+          const float4 w4 = *reinterpret_cast<const float4*>(wsrc + col);
+          const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+          bf16x4 o4;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            o4[r] = static_cast<__bf16>(__builtin_fmaf(coef * wv[r], float(l4[r]), acc[db][g4 * 4 + r] * scale));
+          *reinterpret_cast<bf16x4*>(dst + col) = o4;
+        }
       }
     }
     if (p.lse != nullptr && hh == 0) {

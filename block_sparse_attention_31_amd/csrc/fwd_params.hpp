@@ -46,6 +46,14 @@ struct FwdParams {
   int32_t per_xcd;         // ceil(total_tiles / 8)
   int32_t split_tail;      // trailing tiles of each XCD's share run as two halves
   int32_t deal;            // piles each (sample, head)'s tile list is dealt into
+  // Optional two-branch fusion in the epilogue (bf16 kernel; lin == nullptr
+  // turns it off): out = softmax branch + sigmoid(gate_lin) * lin * lin_w /
+  // sqrt(sum_h lin_ss / (H*D) + lin_eps).
+  const void* lin;         // [B,S,H,D] bf16 linear-branch output
+  const float* lin_ss;     // [B,S,H] per (token, head) sum of squares of lin
+  const float* gate_lin;   // [B,S,H] linear-branch gate logits
+  const float* lin_w;      // [H*D] RMSNorm weight
+  float lin_eps;
   QBlockDesc blk[kMaxQueryBlocks];
 };
 

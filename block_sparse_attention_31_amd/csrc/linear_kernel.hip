@@ -353,6 +353,7 @@ __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(
   const int64_t bh_off = int64_t(b) * p.S * rs + int64_t(h) * D;
   __bf16* __restrict__ og = static_cast<__bf16*>(p.out) + bh_off;
 
+  float* __restrict__ ssg = p.ss == nullptr ? nullptr : p.ss + int64_t(b) * p.S * p.H + h;
   if (beta < 0 || linear_frames(beta, p.F, p.Bf) == 0) {
     // text rows, or a block with no linear keys: zeros
     const int n = (r_hi - r_lo) * CH;
@@ -360,6 +361,8 @@ __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(
       const int r = r_lo + c / CH;
       *reinterpret_cast<u32x4*>(og + int64_t(r) * rs + (c % CH) * 8) = u32x4{0u, 0u, 0u, 0u};
     }
+    if (ssg != nullptr)
+      for (int r = r_lo + int(threadIdx.x); r < r_hi; r += NW * 64) ssg[int64_t(r) * p.H] = 0.f;
     return;
   }
 
@@ -434,6 +437,7 @@ __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(
     // the 8-byte writes of 32 rows meet at most two to a bank, the row reads
     // not at all.
     char* os = Os[wave];
+    float ssq = 0.f;  // this lane's half of the row's sum of squares
 #pragma unroll
     for (int pair = 0; pair < NDB / 2; ++pair) {
 #pragma unroll
@@ -443,7 +447,11 @@ __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(
         for (int g4 = 0; g4 < 4; ++g4) {
           bf16x4 o4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[4 * g4 + r] * inv);
+          for (int r = 0; r < 4; ++r) {
+            const float x = acc[4 * g4 + r] * inv;
+            ssq = __builtin_fmaf(x, x, ssq);
+            o4[r] = static_cast<__bf16>(x);
+          }
           const int ch = (4 * dd + g4) ^ ((lr >> 1) & 7);
           *reinterpret_cast<bf16x4*>(os + lr * 128 + ch * 16 + hh * 8) = o4;
         }
@@ -456,8 +464,15 @@ __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(
         if (orow < r_hi) *reinterpret_cast<u32x4*>(og + int64_t(orow) * rs + pair * 64 + pc * 8) = v;
       }
     }
+    if (ssg != nullptr) {
+      ssq = xhalf_sum(ssq);
+      const int row = r_lo + 32 * g + lr;
+      if (hh == 0 && row < r_hi) ssg[int64_t(row) * p.H] = ssq;
+    }
 #else
+    const int row = r_lo + 32 * g + lr;
     __bf16* dst = og + int64_t(row) * rs;
+    float ssq = 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const f32x16 acc = block(db);
@@ -466,10 +481,18 @@ __global__ __launch_bounds__(NW * 64, VDN_LIN_APPLY_MINW) void lin_apply_kernel(
         for (int g4 = 0; g4 < 4; ++g4) {
           bf16x4 o4;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[4 * g4 + r] * inv);
+          for (int r = 0; r < 4; ++r) {
+            const float x = acc[4 * g4 + r] * inv;
+            ssq = __builtin_fmaf(x, x, ssq);
+            o4[r] = static_cast<__bf16>(x);
+          }
           *reinterpret_cast<bf16x4*>(dst + 32 * db + 8 * g4 + 4 * hh) = o4;
         }
       }
+    }
+    if (ssg != nullptr) {
+      ssq = xhalf_sum(ssq);
+      if (hh == 0 && row < r_hi) ssg[int64_t(row) * p.H] = ssq;
     }
 #endif
   }

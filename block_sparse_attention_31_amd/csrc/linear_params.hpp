@@ -21,6 +21,8 @@ struct LinParams {
                    // ([d2][d1], fp32) followed by sum_t phi(k) ([d1])
   void* bstate;    // workspace [B*H][nb][D*D] bf16: per-block state, [d2][d1]
   float* bz;       // workspace [B*H][nb][D] fp32: per-block normaliser
+  float* ss;       // optional [B,S,H] fp32: sum over d of each output row's
+                   // squares (before rounding to bf16), or nullptr
   int32_t B, S, H, F, T, Bf, nb;
   int32_t tiles_per_block;  // apply tiles of a full frame block
   int32_t tiles_last;       // apply tiles of the last frame block

@@ -208,6 +208,50 @@ int vdn_hybrid_fuse(const void* soft_out, const void* lin_out,
                     void* hip_stream);
 
 /*
+ * The hybrid attention output in one call, asynchronous on `hip_stream`: the
+ * complement linear branch of q, k, v (as vdn_linear_branch_fwd), then the
+ * local softmax branch (as vdn_local_attn_fwd, bf16) whose epilogue adds the
+ * linear branch exactly as vdn_hybrid_fuse does (openi.cn "VDN-MiniMax-H3",
+ * section "technical principles"):
+ *
+ *   out[t] = softmax branch with its gate[t]
+ *            + sigmoid(gate_lin[t, h]) * lin[t] * norm_weight
+ *              / sqrt(mean(lin[t]^2) + eps),
+ *
+ * summed in fp32 and rounded to bf16 once (the two-call path rounds the
+ * softmax branch first).  The mean of squares comes from the linear branch's
+ * values before their rounding.
+ *
+ *   q, k, v, gate, F .. block_frames, heads, head_dim, batch, softmax_scale,
+ *   lse      as for vdn_local_attn_fwd (bf16, head_dim 64 or 128; gate and
+ *            lse may be NULL).
+ *   gate_lin device fp32 [batch, S, heads] logits of the linear branch's gate.
+ *   norm_weight device fp32 [heads * head_dim], 16-byte aligned.
+ *   eps      finite, >= 0.
+ *   out      device, [batch, S, heads, head_dim] bfloat16.
+ *   workspace device, caller-owned, at least vdn_hybrid_attn_workspace_bytes
+ *            bytes, 256-byte aligned; holds the linear branch's states, its
+ *            output and its per-(token, head) sums of squares.
+ * Validation before any HIP call; no allocation, no synchronisation.  The
+ * workspace must not overlap any input or output, and out and lse must not
+ * overlap gate_lin or norm_weight.
+ */
+int vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v,
+                        const float* gate, const float* gate_lin,
+                        const float* norm_weight, float eps, void* out,
+                        int F, int tokens_per_frame, int n_text,
+                        int block_frames, int heads, int head_dim, int batch,
+                        float softmax_scale, float* lse, void* workspace,
+                        int64_t workspace_bytes, void* hip_stream);
+
+/* Host only.  Workspace bytes vdn_hybrid_attn_fwd needs for this shape (the
+ * linear branch's, plus batch * S * heads * (2 * head_dim + 4), each part
+ * rounded up to 256 bytes), or a negative vdn_status_t. */
+int64_t vdn_hybrid_attn_workspace_bytes(int F, int tokens_per_frame,
+                                        int n_text, int block_frames,
+                                        int heads, int head_dim, int batch);
+
+/*
  * Host only.  Number of query blocks for a geometry: ceil(F/block_frames)
  * frame blocks, plus one text block when n_text > 0.  Returns the count
  * (>= 1) or a negative vdn_status_t.

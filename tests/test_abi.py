@@ -274,3 +274,55 @@ def test_fuse_zero_tokens_is_a_no_op(L):
     a = fuse_args(tokens=0)
     rc = L.vdn_hybrid_fuse(a["soft"], a["lin"], a["gate"], a["w"], a["eps"], a["out"], 0, a["H"], a["D"], None)
     assert rc == 0
+
+
+# ------------------------------------------------ hybrid attention in one call
+
+
+@pytest.mark.parametrize("F,T,N,Bf", SWEEP[::7])
+@pytest.mark.parametrize("H,D,batch", [(32, 128, 1), (2, 64, 3)])
+def test_hybrid_workspace_bytes(L, F, T, N, Bf, H, D, batch):
+    # the linear branch's workspace, then its bf16 output and one fp32 sum of
+    # squares per (token, head), each rounded up to 256 bytes
+    rows = batch * (F * T + N) * H
+    want = (_up256(B.vdn_linear_branch_workspace_bytes(F, T, N, Bf, H, D, batch))
+            + _up256(rows * D * 2) + _up256(rows * 4))
+    assert B.vdn_hybrid_attn_workspace_bytes(F, T, N, Bf, H, D, batch) == want
+
+
+def hyb_args(**kw):
+    args = dict(q=A, k=A + STEP, v=A + 2 * STEP, gate=A + 3 * STEP, gate_lin=A + 4 * STEP,
+                w=A + 5 * STEP, eps=1e-6, out=A + 6 * STEP, F=20, T=1008, N=512, Bf=5, H=32, D=128,
+                batch=1, scale=0.0, lse=A + 7 * STEP, ws=A + 8 * STEP, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return args
+
+
+HYB_ERRORS = [
+    ("F=0", dict(F=0), -1),
+    ("head_dim 96", dict(D=96), -2),
+    ("gate_lin NULL", dict(gate_lin=None), -1),
+    ("norm_weight NULL", dict(w=None), -1),
+    ("workspace NULL", dict(ws=None), -1),
+    ("eps negative", dict(eps=-1.0), -1),
+    ("eps NaN", dict(eps=float("nan")), -1),
+    ("workspace small", dict(ws_bytes=1 << 20), -1),
+    ("workspace misaligned", dict(ws=A + 8 * STEP + 64), -3),
+    ("norm_weight misaligned", dict(w=A + 5 * STEP + 4), -3),
+    ("gate_lin misaligned", dict(gate_lin=A + 4 * STEP + 2), -3),
+    ("workspace over q", dict(ws=A + 1024), -1),
+    ("workspace over out", dict(ws=A + 6 * STEP - 4096), -1),
+    ("out over norm_weight", dict(out=A + 5 * STEP - 4096), -1),
+    ("q NULL", dict(q=None), -1),
+    ("q misaligned", dict(q=A + 8), -3),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", HYB_ERRORS, ids=[c[0] for c in HYB_ERRORS])
+def test_hybrid_argument_errors(L, name, kw, code):
+    a = hyb_args(**kw)
+    rc = L.vdn_hybrid_attn_fwd(a["q"], a["k"], a["v"], a["gate"], a["gate_lin"], a["w"], a["eps"],
+                               a["out"], a["F"], a["T"], a["N"], a["Bf"], a["H"], a["D"], a["batch"],
+                               a["scale"], a["lse"], a["ws"], a["ws_bytes"], a["stream"])
+    assert rc == code, (name, rc, B.vdn_last_error())
+    assert B.vdn_last_error() != ""

@@ -266,3 +266,39 @@ def test_hybrid_end_to_end():
                              fi["weight"].to(torch.float64).numpy(), 1e-6)
     check("hybrid end to end", out.cpu().to(torch.float64).numpy(), ref)
     assert math.isfinite(float(out.float().abs().max()))
+
+
+@pytest.mark.parametrize("kw", [dict(B=1, H=2, D=128, F=16, T=40, N=12, Bf=5, gate=True),
+                                dict(B=2, H=3, D=64, F=11, T=33, N=5, Bf=2, gate=False),
+                                dict(B=1, H=4, D=128, F=3, T=20, N=40, Bf=1, gate=True)])
+def test_hybrid_one_call(kw):
+    # the whole hybrid output from vdn_hybrid_attn_fwd (fusion in the softmax
+    # branch's epilogue) against the oracle chain, and against the three-call
+    # path (which rounds the softmax branch before the sum); the workspace
+    # starts as 0xFF bytes and out as NaN, so stale or unwritten data shows
+    w = synth.random_workload(781 + kw["F"], **kw)
+    inp = synth.make_inputs(w)
+    v = synth.with_frame_offsets(inp["v"], w.F, w.T, 0.2)
+    fi = synth.make_fuse_inputs(w)
+    q, k, vd = (t.to(DEV) for t in (inp["q"], inp["k"], v))
+    g = None if inp["gate"] is None else inp["gate"].to(DEV)
+    gl, wt = fi["gate"].to(DEV), fi["weight"].to(DEV)
+    n = B.vdn_hybrid_attn_workspace_bytes(w.F, w.T, w.N, w.Bf, w.H, w.D, w.B)
+    ws = torch.full((n,), 255, dtype=torch.uint8, device=DEV)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=DEV)
+    B.vdn_hybrid_attn_fwd(q, k, vd, g, gl, wt, out, w.F, w.T, w.N, w.Bf, eps=1e-6, lse=lse, workspace=ws)
+    soft = B.local_attn_fwd(q, k, vd, g, F=w.F, tokens_per_frame=w.T, n_text=w.N, block_frames=w.Bf)
+    lin = B.linear_branch_fwd(q, k, vd, F=w.F, tokens_per_frame=w.T, n_text=w.N, block_frames=w.Bf)
+    three = B.hybrid_fuse(soft, lin, gl, wt, 1e-6)
+    torch.cuda.synchronize()
+    got = out.cpu().to(torch.float64).numpy()
+    qn, kn, vn, gn = oracle_inputs({"q": inp["q"], "k": inp["k"], "v": v, "gate": inp["gate"], "scales": None})
+    soft_ref, lse_ref = oracle.attend(qn, kn, vn, gn, w.F, w.T, w.N, w.Bf)
+    lin_ref = oracle.linear_branch(qn, kn, vn, w.F, w.T, w.N, w.Bf)
+    ref = oracle.hybrid_fuse(soft_ref, lin_ref, fi["gate"].to(torch.float64).numpy(),
+                             fi["weight"].to(torch.float64).numpy(), 1e-6)
+    check("hybrid one call", got, ref)
+    check("hybrid one call vs three calls", got, three.cpu().to(torch.float64).numpy())
+    # the log-sum-exp output is the softmax branch's
+    assert np.max(np.abs(lse.cpu().numpy() - lse_ref)) <= 2e-3
