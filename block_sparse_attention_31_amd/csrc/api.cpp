@@ -194,7 +194,7 @@ static int local_attn_fwd_impl(const void* q, const void* k, const void* v, cons
                                void* out, int F, int tokens_per_frame, int n_text, int block_frames,
                                int heads, int head_dim, int dtype, int batch,
                                const float* qkv_scales, float softmax_scale, float* lse,
-                               void* hip_stream, const FuseArgs* fuse) {
+                               void* hip_stream, const FuseArgs* fuse, bool validate_only = false) {
   vdn::Geometry g;
   std::string err;
   if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
@@ -286,6 +286,7 @@ static int local_attn_fwd_impl(const void* q, const void* k, const void* v, cons
   p.tiles_per_bh = prefix;
   p.total_tiles = prefix * batch * heads;
   set_dispatch(p);
+  if (validate_only) return ok();
   if (fuse != nullptr) {
     p.lin = fuse->lin;
     p.lin_ss = fuse->ss;
@@ -603,13 +604,21 @@ int vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const float
     if (overlaps(out, t_bytes, x.p, x.n) || (lse != nullptr && overlaps(lse, l_bytes, x.p, x.n)))
       return fail(VDN_ERR_INVALID_ARG, "out or lse overlaps gate_lin or norm_weight");
 
+  // the softmax branch's arguments are checked before the linear branch is
+  // launched, so that a failing call launches nothing
+  const FuseArgs probe{nullptr, nullptr, gate_lin, norm_weight, eps};
+  int rc = local_attn_fwd_impl(q, k, v, gate, out, F, tokens_per_frame, n_text, block_frames, heads,
+                               head_dim, VDN_BF16, batch, nullptr, softmax_scale, lse, hip_stream,
+                               &probe, true);
+  if (rc != 0) return rc;
+
   // workspace: the linear branch's own, then its output, then the per
   // (token, head) sums of squares of that output
   char* ws = static_cast<char*>(workspace);
   void* lin_out = ws + up256(uint64_t(lin_need));
   float* row_ss = reinterpret_cast<float*>(ws + up256(uint64_t(lin_need)) + up256(uint64_t(t_bytes)));
-  int rc = linear_branch_fwd_impl(q, k, v, lin_out, F, tokens_per_frame, n_text, block_frames, heads,
-                                  head_dim, batch, ws, lin_need, hip_stream, row_ss);
+  rc = linear_branch_fwd_impl(q, k, v, lin_out, F, tokens_per_frame, n_text, block_frames, heads,
+                              head_dim, batch, ws, lin_need, hip_stream, row_ss);
   if (rc != 0) return rc;
   const FuseArgs fuse{lin_out, row_ss, gate_lin, norm_weight, eps};
   return local_attn_fwd_impl(q, k, v, gate, out, F, tokens_per_frame, n_text, block_frames, heads,

@@ -315,6 +315,12 @@ HYB_ERRORS = [
     ("out over norm_weight", dict(out=A + 5 * STEP - 4096), -1),
     ("q NULL", dict(q=None), -1),
     ("q misaligned", dict(q=A + 8), -3),
+    # the softmax branch's own arguments, checked before the linear branch is
+    # launched (a launch here, without a GPU, would report a HIP error)
+    ("lse misaligned", dict(lse=A + 7 * STEP + 2), -3),
+    ("gate misaligned", dict(gate=A + 3 * STEP + 2), -3),
+    ("softmax_scale NaN", dict(scale=float("nan")), -1),
+    ("out aliases q", dict(out=A), -1),
 ]
 
 
