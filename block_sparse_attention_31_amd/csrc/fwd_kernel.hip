@@ -50,7 +50,7 @@ namespace vdn {
 // 16 lanes, lane i receives element (i % 4) of the 8-byte blocks addressed by
 // lanes 4e + i/4 (e = 0..3), so if those lanes point at keys k+e, columns
 // d0 + 4(i/4).., lane i holds V[k..k+3][d0 + i]: the MFMA A-operand layout.
-template <int D, int NW, int NS, int KT, int KPF, int VPF>
+template <int D, int NW, int NS, int KT, int KPF, int VPF, bool FUSE>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int QW = 32;          // query rows per wave
@@ -65,6 +65,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   constexpr int NKB = KT / 32;    // 32-key blocks per step
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
   static_assert(NS == 2 || NS == 4, "the main loop is unrolled for a 2- or 4-stage ring");
+  static_assert(!FUSE || (NS == 2 && NW == 8 && TILE >= 4 * 32 * RB),
+                "the fused epilogue stages each wave's 32 linear rows in the two free ring stages");
   // V row swizzle: whole groups of four 16-byte chunks move with key % 4, so
   // the 32 lanes of a transposing read (4 keys x 32 columns) cover all banks.
   auto vswz = [](int r) { return (4 * (r & 3)) % CH; };
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // its gate over the token's RMS (from the per-head sums of squares), read
   // here so that its loads overlap Q's.
   float lin_coef = 0.f;
-  if (p.lin != nullptr) {
+  if constexpr (FUSE) {
     const int lrow = wave * QW + lr;
     if (lrow < rows) {
       const int64_t tok = int64_t(b) * p.S + row0 + lrow;
@@ -349,10 +351,32 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // exactly one batch (past the end of the key list a harmless re-fetch
   // of the last key into the free stage), so the wait count is the same
   // on every step.
-  auto body = [&](int step, auto stage_c) {
+  // With the fused epilogue, the last step brings this wave's 32 rows of the
+  // linear-branch output into the free stage pair instead of re-fetching past
+  // the end of the key list (waves 0-3 into the K stage, 4-7 into the V
+  // stage, 32 rows each; 16-byte chunk c of row r at c ^ (r % CH)).
+  auto lin_stage = [&](auto stage_c) -> char* {
+    return wave < 4 ? kstage(stage_c) + wave * 32 * RB : vstage(stage_c) + (wave - 4) * 32 * RB;
+  };
+  auto issue_lin = [&](char* dst) {
+    const char* lg = static_cast<const char*>(p.lin) + bh_off * 2;
+#pragma unroll
+    for (int i = 0; i < 32 * RB / 1024; ++i) {
+      const int r = i * RPI + lane / CH, c = (lane % CH) ^ (r % CH);
+      const int grow = row0 + min(wave * QW + r, rows - 1);
+      lds_dma16(lg + int64_t(grow) * rsb + c * 16, dst + i * 1024);
+    }
+  };
+  // one step; `last` (compile-time) makes it the fused kernel's last step,
+  // which brings in the linear rows instead of re-fetching past the end
+  auto body = [&](int step, auto stage_c, auto last_c) {
     constexpr int st = decltype(stage_c)::value;
-    issue(step + NS - 1, kstage(IC<(st + NS - 1) % NS>{}), IC<1>{});
-    issue(step + NS - 1, vstage(IC<(st + NS - 1) % NS>{}), IC<0>{});
+    if constexpr (decltype(last_c)::value != 0) {
+      issue_lin(lin_stage(IC<(st + NS - 1) % NS>{}));
+    } else {
+      issue(step + NS - 1, kstage(IC<(st + NS - 1) % NS>{}), IC<1>{});
+      issue(step + NS - 1, vstage(IC<(st + NS - 1) % NS>{}), IC<0>{});
+    }
     if (active) {
       f32x16 s[NKB];
       qk(kstage(stage_c), s);
@@ -379,16 +403,31 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
   lds_barrier();
-  for (int step = 0;;) {
-    body(step, IC<0>{});
-    if (++step >= nsteps) break;
-    body(step, IC<1 % NS>{});
-    if (++step >= nsteps) break;
-    if constexpr (NS > 2) {
-      body(step, IC<2 % NS>{});
+  if constexpr (!FUSE) {
+    for (int step = 0;;) {
+      body(step, IC<0>{}, IC<0>{});
       if (++step >= nsteps) break;
-      body(step, IC<3 % NS>{});
+      body(step, IC<1 % NS>{}, IC<0>{});
       if (++step >= nsteps) break;
+      if constexpr (NS > 2) {
+        body(step, IC<2 % NS>{}, IC<0>{});
+        if (++step >= nsteps) break;
+        body(step, IC<3 % NS>{}, IC<0>{});
+        if (++step >= nsteps) break;
+      }
+    }
+  } else {
+    // the same loop with the last step (nsteps >= 1) taken out of it
+    int step = 0;
+    for (; step + 2 < nsteps; step += 2) {
+      body(step, IC<0>{}, IC<0>{});
+      body(step + 1, IC<1>{}, IC<0>{});
+    }
+    if (step + 2 == nsteps) {
+      body(step, IC<0>{}, IC<0>{});
+      body(step + 1, IC<1>{}, IC<1>{});
+    } else {
+      body(step, IC<0>{}, IC<1>{});
     }
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA outlives the workgroup
@@ -405,7 +444,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       scale *= 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
     }
     __bf16* dst = og + int64_t(row) * rs;
-    if (p.lin == nullptr) {
+    if constexpr (!FUSE) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -421,14 +460,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       // linear-branch row, scaled by its factor and the norm weight, joins
       // this row
       const float coef = lin_coef;
-      const __bf16* lsrc = static_cast<const __bf16*>(p.lin) + bh_off + int64_t(row) * rs;
+      // the row landed in LDS with the last step (stage (nsteps - 1 + NS - 1)
+      // % NS, the one the last step did not read)
+      const char* lrow_lds = ((nsteps - 1) % NS == 0 ? lin_stage(IC<1 % NS>{}) : lin_stage(IC<0>{})) + lr * RB;
       const float* wsrc = p.lin_w + h * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int col = db * 32 + g4 * 8 + hh * 4;
-          const bf16x4 l4 = *reinterpret_cast<const bf16x4*>(lsrc + col);
+          const int c = (db * 4 + g4) ^ (lr % CH);
+          const bf16x4 l4 = *reinterpret_cast<const bf16x4*>(lrow_lds + c * 16 + hh * 8);
           const float4 w4 = *reinterpret_cast<const float4*>(wsrc + col);
           const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
           bf16x4 o4;
@@ -482,9 +524,15 @@ int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
   if (dtype == 1) return launch_fwd_fp8(p, head_dim, stream);
   if (dtype != 0) return int(hipErrorInvalidValue);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV>), grid, block, 0, st, p);
+    if (p.lin != nullptr)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false>), grid, block, 0, st, p);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV>), grid, block, 0, st, p);
+    if (p.lin != nullptr)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true>), grid, block, 0, st, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
