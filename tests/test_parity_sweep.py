@@ -1,4 +1,5 @@
-"""Seeded sweep of small random shapes through every GPU entry point, each
+"""Seeded sweep of small random shapes through the GPU entry points (softmax
+forward and backward, linear branch, the hybrid output in one call), each
 compared in full with the oracle: batches of one or two samples, one to five
 heads, both head sizes, ragged frames, videos shorter than a block, no text
 or more text than video, one-frame blocks.  Shapes this small give each XCD
@@ -7,14 +8,17 @@ tiles."""
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
+from block_sparse_attention_31_amd import binding as B
 from block_sparse_attention_31_amd import synth
 
 from .gpu_util import BF16_LSE_BOUND, compare, gpu_available, oracle_inputs, run_gpu
 from .test_parity_bwd import _oracle as bwd_oracle
 from .test_parity_bwd import check as bwd_check
 from .test_parity_bwd import run_bwd
+from .test_parity_linear import DEV
 from .test_parity_linear import check as lin_check
 from .test_parity_linear import inputs as lin_inputs
 from .test_parity_linear import oracle_linear, run_linear, zero_rows
@@ -41,6 +45,7 @@ def _shapes(n, seed, max_s):
 FWD = _shapes(40, 9001, 700)
 BWD = _shapes(20, 9002, 500)
 LIN = _shapes(20, 9003, 700)
+HYB = _shapes(20, 9004, 600)
 
 
 def _name(s):
@@ -77,3 +82,22 @@ def test_sweep_linear(s):
         lin_check(_name(s), got, ref)
     else:
         assert np.all(got == 0.0)
+
+
+@pytest.mark.parametrize("s", HYB, ids=[_name(s) for s in HYB])
+def test_sweep_hybrid_one_call(s):
+    w = synth.random_workload(seed=9400 + s["F"] * 13 + s["T"], **s)
+    inp = synth.make_inputs(w)
+    v = synth.with_frame_offsets(inp["v"], w.F, w.T, 0.2)
+    fi = synth.make_fuse_inputs(w)
+    q, k, vd = (t.to(DEV) for t in (inp["q"], inp["k"], v))
+    g = None if inp["gate"] is None else inp["gate"].to(DEV)
+    out = B.hybrid_attn_fwd(q, k, vd, g, fi["gate"].to(DEV), fi["weight"].to(DEV), F=w.F,
+                            tokens_per_frame=w.T, n_text=w.N, block_frames=w.Bf, eps=1e-6)
+    torch.cuda.synchronize()
+    qn, kn, vn, gn = oracle_inputs({"q": inp["q"], "k": inp["k"], "v": v, "gate": inp["gate"], "scales": None})
+    soft_ref, _ = oracle.attend(qn, kn, vn, gn, w.F, w.T, w.N, w.Bf)
+    lin_ref = oracle.linear_branch(qn, kn, vn, w.F, w.T, w.N, w.Bf)
+    ref = oracle.hybrid_fuse(soft_ref, lin_ref, fi["gate"].to(torch.float64).numpy(),
+                             fi["weight"].to(torch.float64).numpy(), 1e-6)
+    lin_check(_name(s), out.cpu().to(torch.float64).numpy(), ref)
