@@ -25,6 +25,11 @@
 //   B), A = V^T fragments from transposing LDS reads of row-major V.  The
 //   accumulator again has one query per lane, so the online-softmax rescale
 //   is a per-lane scalar multiply.
+//
+// Fused instance (FUSE): the same kernel also adds the linear branch's gated,
+// RMS-normalised output row before the one rounding (openi.cn "VDN-MiniMax-
+// H3", technical principles: the branches are summed after the linear one's
+// RMSNorm and gate); its rows come into LDS with the last step.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
