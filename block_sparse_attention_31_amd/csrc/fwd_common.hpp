@@ -84,6 +84,10 @@ __device__ __forceinline__ int interval_delta(const KeyList& k, int j) {
 // the base-2 domain: P then stays below 256, exact in bf16 up to rounding,
 // and the accumulator rescale is skipped unless the maximum grows by more.
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f;
+// With the reference point fixed per row, it is set this far (log2 units)
+// above the row's first-step maximum: later keys may then exceed that
+// maximum by up to 48 before a weight passes 2^32.
+[[maybe_unused]] constexpr float kRefHeadroom = 16.0f;
 
 template <int N>
 using IC = std::integral_constant<int, N>;
@@ -128,23 +132,21 @@ __device__ __forceinline__ TileSlot tile_slot(int w, int per_xcd, int split) {
 
 // Sets the scores of keys past the end of the key list to -inf on a partial
 // last step.  Score register (kb, r) of a 32x32 MFMA result holds key
-// 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 of the step; `lim` (wave-uniform)
-// is the number of valid keys in the step.  The mask is a min with +-inf:
-// (rem - offset - 1/2) is never zero, so its product with +inf is +inf for a
-// valid key and -inf past the end.  Written without compares (each would
-// produce a 64-bit lane mask in scalar registers, which the compiler keeps
-// alive side by side) and without integer bit operations on the scores
-// (which this compiler fuses into wrong three-input bit operations).
+// 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 of the step, so in each lane the
+// keys rise with the register index e = 16 kb + r and the valid ones (below
+// `lim`, wave-uniform) form a prefix of the lane's registers, of length
+// 4 floor(y / 8) + min(4, y % 8) with y = lim - 4 (lane / 32).  One integer
+// compare of e (an inline constant) against that length per register: no
+// per-register float constants for the compiler to materialise.
 template <int NKB>
 __device__ __forceinline__ void mask_tail(f32x16 (&s)[NKB], int lim, int hh) {
-  const float rem = float(lim - 4 * hh);
+  const int y = lim - 4 * hh;
+  const int nv = y <= 0 ? 0 : 4 * (y >> 3) + min(4, y & 7);
+  const float ninf = -__builtin_inff();
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float off = float(kb * 32 + 8 * (r >> 2) + (r & 3)) + 0.5f;
-      s[kb][r] = fminf(s[kb][r], (rem - off) * __builtin_inff());
-    }
+    for (int r = 0; r < 16; ++r) s[kb][r] = kb * 16 + r < nv ? s[kb][r] : ninf;
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
@@ -173,7 +175,16 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
 __device__ __forceinline__ void lds_dma16(const char* sbase, uint32_t voff, const char* lds) {
 #if VDN_ASM_DMA
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>(lds)));
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+  // the base is wave-uniform by contract; saying so keeps it in scalar
+  // registers where the compiler cannot prove it (free where it can)
+  const uint64_t a = reinterpret_cast<uintptr_t>(sbase);
+  // (the builtin returns int: both halves go through uint32_t, or the low
+  // word would be sign-extended into the high one)
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a >> 32)));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(a)));
+  const uint64_t su = (uint64_t(hi) << 32) | uint64_t(lo);
+  const char* sb = reinterpret_cast<const char*>(su);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sb), "{m0}"(m0) : "memory");
 #else
   __builtin_amdgcn_global_load_lds(sbase + voff, VDN_LDS(lds), 16, 0, 0);
 #endif

@@ -39,6 +39,10 @@
 #ifndef VDN_PIN_QK
 #define VDN_PIN_QK 1
 #endif
+// row sums by bf16 dot products over the rounded weights (1) or fp32 adds (0)
+#ifndef VDN_ROWSUM_DOT
+#define VDN_ROWSUM_DOT 0
+#endif
 
 namespace vdn {
 
@@ -55,7 +59,7 @@ namespace vdn {
 // 16 lanes, lane i receives element (i % 4) of the 8-byte blocks addressed by
 // lanes 4e + i/4 (e = 0..3), so if those lanes point at keys k+e, columns
 // d0 + 4(i/4).., lane i holds V[k..k+3][d0 + i]: the MFMA A-operand layout.
-template <int D, int NW, int NS, int KT, int KPF, int VPF, bool FUSE>
+template <int D, int NW, int NS, int KT, int KPF, int VPF, bool FUSE, bool FIXREF>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   constexpr int QW = 32;          // query rows per wave
@@ -70,6 +74,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   constexpr int NKB = KT / 32;    // 32-key blocks per step
   static_assert(NI >= 1 && NI * NW * 1024 == TILE, "tile shape");
   static_assert(NS == 2 || NS == 4, "the main loop is unrolled for a 2- or 4-stage ring");
+  static_assert(!FIXREF || NS == 2, "the fixed-reference loop is unrolled for a 2-stage ring");
   static_assert(!FUSE || (NS == 2 && NW == 8 && TILE >= 4 * 32 * RB),
                 "the fused epilogue stages each wave's 32 linear rows in the two free ring stages");
   // V row swizzle: whole groups of four 16-byte chunks move with key % 4, so
@@ -172,50 +177,49 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // ---- DMA addressing.  Instruction i of this wave covers key rows
   // dma_row[i] .. (RPI rows per instruction); lane -> (row, physical chunk);
   // it fetches the logical chunk that the swizzle stores there.
-  int dma_row[NI];
-  uint32_t k_goff[NI], v_goff[NI];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int q = wave * NI + i;
-    const int r = q * RPI + lane / CH;
-    const int pc = lane % CH;
-    dma_row[i] = r;
-    k_goff[i] = uint32_t(r * rsb + ((pc ^ (r % CH)) * 16));
-    v_goff[i] = uint32_t(r * rsb + ((pc ^ vswz(r)) * 16));
-  }
+  // Row of instruction i is r0 + i RPI.  The K swizzle XORs the chunk with
+  // r % CH = (r0 % CH) ^ ((i RPI) % CH) (r0 % CH < RPI, so no carry), the V
+  // swizzle depends on r % 4 = r0 % 4 only; so one lane offset per tensor
+  // serves every instruction: instruction i adds i RPI rows through the
+  // scalar base and, for K, XORs a constant into the chunk.
+  const int r0 = wave * NI * RPI + lane / CH;
+  const uint32_t k_chunk0 = uint32_t(((lane % CH) ^ (r0 % CH)) * 16);
+  const uint32_t v_chunk0 = uint32_t(((lane % CH) ^ vswz(r0)) * 16);
+  auto kx = [](int i) { return uint32_t(((i * RPI) % CH) * 16); };
 
   // Addresses of one step's keys: a scalar base when the step lies inside
   // one key interval, else key by key (rows past the end of the key list are
   // clamped to its last key and masked out of the softmax).
-  // (the tensor is a compile-time tag: choosing between the two offset arrays
-  // at run time would force them out of registers)
-  auto issue = [&](int step, char* lbase, auto is_k_c) {
+  // (the tensor is a compile-time tag)
+  auto issue = [&](int step, char* lbase, auto is_k_c) __attribute__((always_inline)) {
     constexpr bool is_k = decltype(is_k_c)::value != 0;
-    uint32_t goff[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if constexpr (is_k) {
-        goff[i] = k_goff[i];
-      } else {
-        goff[i] = v_goff[i];
-      }
-    }
     const char* gbase = is_k ? kg : vg;
+    const uint32_t chunk0 = is_k ? k_chunk0 : v_chunk0;
     const int j0 = step * KT;
     // interval holding j0, its end and offset (scalar selects)
     const int iv_end = interval_end(kl, j0);
     const int delta = interval_delta(kl, j0);
+    // This wave's LDS destination, recomputed at every call (opaque to the
+    // compiler): hoisted, the per-instruction destinations of both stages and
+    // tensors would hold a dozen scalar registers across the loop.
+    uint32_t wdst = uint32_t(wave * NI * 1024);
+    asm volatile("" : "+s"(wdst));
     if (j0 + KT <= iv_end) {
       const char* base = gbase + int64_t(j0 + delta) * rsb;
+      int64_t step_b = int64_t(RPI) * rsb;
+      asm volatile("" : "+s"(step_b));
+      const uint32_t off0 = uint32_t(r0 * rsb) + chunk0;
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        lds_dma16(base, goff[i], lbase + (wave * NI + i) * 1024);
+      for (int i = 0; i < NI; ++i) {
+        lds_dma16(base, is_k ? off0 ^ kx(i) : off0, lbase + wdst + i * 1024);
+        base += step_b;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int j = min(j0 + dma_row[i], n_keys - 1);
-        lds_dma16(gbase + int64_t(vtoken(kl, j)) * rsb + (goff[i] - uint32_t(dma_row[i] * rsb)),
-                  lbase + (wave * NI + i) * 1024);
+        const int j = min(j0 + r0 + i * RPI, n_keys - 1);
+        lds_dma16(gbase + int64_t(vtoken(kl, j)) * rsb + (is_k ? chunk0 ^ kx(i) : chunk0),
+                  lbase + wdst + i * 1024);
       }
     }
   };
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   const bool active = __builtin_amdgcn_readfirstlane(wave) * 32 < rows;
   const float c = p.score_scale_log2;
   const int nsteps = (n_keys + KT - 1) / KT;
-  const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  [[maybe_unused]] const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
   // S^T = K Q^T for the KT keys in K stage `stage_c`.  The K fragments run
   // KPF reads ahead of the MFMAs that consume them (a read issued just
@@ -254,6 +258,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   auto qk = [&](const char* ks, f32x16 (&s)[NKB]) {
     constexpr int NF = NDS * NKB;  // fragments (= MFMAs) per step
     constexpr int PF = KPF < NF ? KPF : NF;
+    // fragment f: key block f % NKB, k-step f / NKB (the NKB accumulators
+    // rotate, so consecutive MFMAs never share one)
     auto frag = [&](int f) {
       return *reinterpret_cast<const bf16x8*>(ks + (f % NKB) * 32 * RB + k_roff(f / NKB));
     };
@@ -329,26 +335,36 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
     }
   };
-  // P = exp2(S c - m), packed to bf16; row sums over the rounded weights.
+  // P = exp2(S c - m), packed to bf16, and its row sum.  The row sum adds
+  // the fp32 weights (two partial sums per lane): the bf16 dot-product form
+  // over the rounded weights issues on the matrix pipe's side of the SIMD
+  // and stalls the MFMAs running beside it, while fp32 adds co-issue.
   auto exp_pack = [&](const f32x16 (&s)[NKB], bf16x8 (&pk)[NKB][2]) {
     const float mneg = -m_run;
-    float lsum = 0.f;
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         bf16x8 v8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v8[e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][half * 8 + e], c, mneg)));
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][half * 8 + e], c, mneg));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][half * 8 + e + 1], c, mneg));
+          v8[e] = static_cast<__bf16>(p0);
+          v8[e + 1] = static_cast<__bf16>(p1);
+#if VDN_ROWSUM_DOT
+          const bf16x2 pr = {v8[e], v8[e + 1]};
+          l0 = __builtin_amdgcn_fdot2_f32_bf16(pr, kOnes2, l0, false);
+#else
+          l0 += p0;
+          l1 += p1;
+#endif
+        }
         pk[kb][half] = v8;
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 0, 1), kOnes2, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 2, 3), kOnes2, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 4, 5), kOnes2, lsum, false);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v8, v8, 6, 7), kOnes2, lsum, false);
       }
     }
-    l_run += lsum;
+    l_run += l0 + l1;
   };
 
   // ---- main loop: per step, S = K Q^T, softmax, O += P V, with the
@@ -372,10 +388,18 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       lds_dma16(lg + int64_t(grow) * rsb + c * 16, dst + i * 1024);
     }
   };
-  // one step; `last` (compile-time) makes it the fused kernel's last step,
-  // which brings in the linear rows instead of re-fetching past the end
-  auto body = [&](int step, auto stage_c, auto last_c) {
+  // One step.  `last` (compile-time) makes it the fused kernel's last step,
+  // which brings in the linear rows instead of re-fetching past the end.
+  // `kind`: kOnline keeps the running maximum (raised by more than the
+  // slack, with a rescale); kFirst sets the reference point of the row to
+  // the step's maximum; kFixed exponentiates against the reference point as
+  // it stands, with no maximum and no branch between the two products.
+  // `tail` (compile-time) allows a partial step (masked past the end of the
+  // key list).
+  constexpr int kOnline = 0, kFirst = 1, kFixed = 2;
+  auto body = [&](int step, auto stage_c, auto last_c, auto kind_c, auto tail_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
+    constexpr int kind = decltype(kind_c)::value;
     if constexpr (decltype(last_c)::value != 0) {
       issue_lin(lin_stage(IC<(st + NS - 1) % NS>{}));
     } else {
@@ -385,9 +409,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     if (active) {
       f32x16 s[NKB];
       qk(kstage(stage_c), s);
-      const int j0 = step * KT;
-      if (j0 + KT > n_keys) mask_tail<NKB>(s, n_keys - j0, hh);
-      rescale(row_max(s));
+      if constexpr (decltype(tail_c)::value != 0) {
+        const int j0 = step * KT;
+        if (j0 + KT > n_keys) mask_tail<NKB>(s, n_keys - j0, hh);
+      }
+      if constexpr (kind == kOnline) {
+        rescale(row_max(s));
+      } else if constexpr (kind == kFirst) {
+        m_run = row_max(s) + kRefHeadroom;
+      }
       bf16x8 pk[NKB][2];
       exp_pack(s, pk);
       pv(vstage(stage_c), pk);
@@ -398,42 +428,101 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     lds_barrier();
   };
   // prologue: steps 0 .. NS-2 in flight
-  issue(0, kstage(IC<0>{}), IC<1>{});
-  issue(0, vstage(IC<0>{}), IC<0>{});
-  if constexpr (NS > 2) {
-    issue(1, kstage(IC<1>{}), IC<1>{});
-    issue(1, vstage(IC<1>{}), IC<0>{});
-    issue(2, kstage(IC<2 % NS>{}), IC<1>{});
-    issue(2, vstage(IC<2 % NS>{}), IC<0>{});
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
-  lds_barrier();
-  if constexpr (!FUSE) {
-    for (int step = 0;;) {
-      body(step, IC<0>{}, IC<0>{});
-      if (++step >= nsteps) break;
-      body(step, IC<1 % NS>{}, IC<0>{});
-      if (++step >= nsteps) break;
-      if constexpr (NS > 2) {
-        body(step, IC<2 % NS>{}, IC<0>{});
+  auto prologue = [&]() __attribute__((always_inline)) {
+    issue(0, kstage(IC<0>{}), IC<1>{});
+    issue(0, vstage(IC<0>{}), IC<0>{});
+    if constexpr (NS > 2) {
+      issue(1, kstage(IC<1>{}), IC<1>{});
+      issue(1, vstage(IC<1>{}), IC<0>{});
+      issue(2, kstage(IC<2 % NS>{}), IC<1>{});
+      issue(2, vstage(IC<2 % NS>{}), IC<0>{});
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * 2 * NI));  // step 0 has landed
+    lds_barrier();
+  };
+  // The whole key list with the online maximum.
+  auto run_online = [&]() __attribute__((always_inline)) {
+    prologue();
+    if constexpr (!FUSE) {
+      for (int step = 0;;) {
+        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
         if (++step >= nsteps) break;
-        body(step, IC<3 % NS>{}, IC<0>{});
+        body(step, IC<1 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
         if (++step >= nsteps) break;
+        if constexpr (NS > 2) {
+          body(step, IC<2 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+          if (++step >= nsteps) break;
+          body(step, IC<3 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+          if (++step >= nsteps) break;
+        }
+      }
+    } else {
+      // the same loop with the last step (nsteps >= 1) taken out of it
+      int step = 0;
+      for (; step + 2 < nsteps; step += 2) {
+        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+        body(step + 1, IC<1>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+      }
+      if (step + 2 == nsteps) {
+        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+        body(step + 1, IC<1>{}, IC<1>{}, IC<kOnline>{}, IC<1>{});
+      } else {
+        body(step, IC<0>{}, IC<1>{}, IC<kOnline>{}, IC<1>{});
       }
     }
-  } else {
-    // the same loop with the last step (nsteps >= 1) taken out of it
-    int step = 0;
-    for (; step + 2 < nsteps; step += 2) {
-      body(step, IC<0>{}, IC<0>{});
-      body(step + 1, IC<1>{}, IC<0>{});
-    }
-    if (step + 2 == nsteps) {
-      body(step, IC<0>{}, IC<0>{});
-      body(step + 1, IC<1>{}, IC<1>{});
+  };
+  // Every row's weights are exponentiated against a fixed reference point.
+  // It starts kRefHeadroom above the row's first-step maximum, so the row
+  // sum is at least 2^-kRefHeadroom and a weight lost to underflow
+  // (< 2^-126) is below 2^-110 of the largest.  Results are exact up to
+  // rounding unless a later key exceeds the point by so much that a weight
+  // overflows: a row sum above 2^32 (no weight above it, no sum near the
+  // fp32 range) sends the workgroup through the key list again.
+  __shared__ int redo;
+  auto vote_redo = [&]() __attribute__((always_inline)) {
+    const float l_chk = xhalf_sum(l_run);
+    const bool bad = wave * QW + lr < rows && !(l_chk <= 0x1p32f);
+    if (tid == 0) redo = 0;
+    lds_barrier();
+    if (__any(bad) && lane == 0) redo = 1;
+    lds_barrier();
+    const bool again = __builtin_amdgcn_readfirstlane(redo) != 0;
+    lds_barrier();  // every wave has read the flag before it is reset or the ring refills
+    return again;
+  };
+  auto reset = [&]() __attribute__((always_inline)) {
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  };
+  if constexpr (FIXREF) {
+    // step 0 sets the reference point (peeled); only the last step can be
+    // partial (peeled; fused, it fetches the linear rows); a rerun takes the
+    // online maximum
+    prologue();
+    if (nsteps == 1) {
+      body(0, IC<0>{}, IC<FUSE ? 1 : 0>{}, IC<kFirst>{}, IC<1>{});
     } else {
-      body(step, IC<0>{}, IC<1>{});
+      body(0, IC<0>{}, IC<0>{}, IC<kFirst>{}, IC<0>{});
+      int step = 1;
+      for (; step + 2 < nsteps; step += 2) {
+        body(step, IC<1>{}, IC<0>{}, IC<kFixed>{}, IC<0>{});
+        body(step + 1, IC<0>{}, IC<0>{}, IC<kFixed>{}, IC<0>{});
+      }
+      if (step + 2 == nsteps) {
+        body(step, IC<1>{}, IC<0>{}, IC<kFixed>{}, IC<0>{});
+        body(step + 1, IC<0>{}, IC<FUSE ? 1 : 0>{}, IC<kFixed>{}, IC<1>{});
+      } else {
+        body(step, IC<1>{}, IC<FUSE ? 1 : 0>{}, IC<kFixed>{}, IC<1>{});
+      }
     }
+    if (vote_redo()) {
+      m_run = -__builtin_inff();
+      reset();
+      run_online();
+    }
+  } else {
+    run_online();
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA outlives the workgroup
 
@@ -515,6 +604,13 @@ constexpr int kReadAhead = VDN_BF16_KPF;  // K fragments in flight ahead of the 
 #define VDN_BF16_VPF 2
 #endif
 constexpr int kReadAheadV = VDN_BF16_VPF;  // V^T fragments in flight ahead of the PV MFMAs
+// Each row's reference point for the exponentials fixed at its first step's
+// maximum (with a range check and an online-maximum rerun), or the online
+// maximum throughout.
+#ifndef VDN_FIXREF
+#define VDN_FIXREF 1
+#endif
+constexpr bool kFixRef = VDN_FIXREF != 0;
 
 int kernel_tile_m(int head_dim, int dtype) {
   (void)head_dim;
@@ -530,14 +626,14 @@ int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
   if (dtype != 0) return int(hipErrorInvalidValue);
   if (head_dim == 128) {
     if (p.lin != nullptr)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true, kFixRef>), grid, block, 0, st, p);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false, kFixRef>), grid, block, 0, st, p);
   } else if (head_dim == 64) {
     if (p.lin != nullptr)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true, kFixRef>), grid, block, 0, st, p);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false>), grid, block, 0, st, p);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false, kFixRef>), grid, block, 0, st, p);
   } else {
     return int(hipErrorInvalidValue);
   }
