@@ -71,6 +71,13 @@ struct FuseArgs {
 
 uint64_t up256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
+// The tiled kernels address the rows of one DMA batch (at most 128 keys or
+// query rows of one (sample, head)) with 32-bit per-lane byte offsets from a
+// scalar base: 128 token strides of heads * head_dim elements must fit.
+bool dma_offsets_fit(int heads, int head_dim, int elem_bytes) {
+  return int64_t(128) * heads * head_dim * elem_bytes < (int64_t(1) << 32);
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,6 +235,8 @@ static int local_attn_fwd_impl(const void* q, const void* k, const void* v, cons
     return fail(VDN_ERR_OVERFLOW, "tensor element count overflows");
   if (int64_t(batch) * heads > INT32_MAX / 4096)
     return fail(VDN_ERR_OVERFLOW, "batch * heads too large");
+  if (!dma_offsets_fit(heads, head_dim, dtype == VDN_BF16 ? 2 : 1))
+    return fail(VDN_ERR_OVERFLOW, "128 token strides of heads * head_dim elements exceed 2^32 bytes");
 
   const size_t in_bytes = size_t(elems) * (dtype == VDN_BF16 ? 2u : 1u);
   const size_t out_bytes = size_t(elems) * 2u;
@@ -343,6 +352,8 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
     return fail(VDN_ERR_OVERFLOW, "tensor element count overflows");
   if (int64_t(batch) * heads > INT32_MAX / 4096)
     return fail(VDN_ERR_OVERFLOW, "batch * heads too large");
+  if (!dma_offsets_fit(heads, head_dim, 2))
+    return fail(VDN_ERR_OVERFLOW, "128 token strides of heads * head_dim elements exceed 2^32 bytes");
 
   const size_t t_bytes = size_t(elems) * 2u;
   const size_t row_bytes = size_t(batch) * size_t(g.S) * size_t(heads) * 4u;
@@ -578,7 +589,9 @@ int vdn_hybrid_attn_fwd(const void* q, const void* k, const void* v, const float
   vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err);
   if (gate_lin == nullptr || norm_weight == nullptr || workspace == nullptr)
     return fail(VDN_ERR_INVALID_ARG, "gate_lin, norm_weight and workspace must be non-NULL");
-  if (!std::isfinite(eps) || eps < 0.f) return fail(VDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  // eps > 0: a token whose linear row is all zeros (text, or a block with no
+  // linear keys) would otherwise scale 0 by 1/sqrt(0)
+  if (!std::isfinite(eps) || !(eps > 0.f)) return fail(VDN_ERR_INVALID_ARG, "eps must be finite and > 0");
   if (workspace_bytes < need)
     return fail(VDN_ERR_INVALID_ARG, "workspace of " + std::to_string(workspace_bytes) + " bytes, " +
                                          std::to_string(need) + " needed");
@@ -634,7 +647,9 @@ int vdn_hybrid_fuse(const void* soft_out, const void* lin_out, const float* gate
     return fail(VDN_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 (got " + std::to_string(head_dim) + ")");
   const int64_t hd = int64_t(heads) * head_dim;
   if (hd > 8192) return fail(VDN_ERR_UNSUPPORTED, "heads * head_dim above 8192");
-  if (!std::isfinite(eps) || eps < 0.f) return fail(VDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  // eps > 0: a token whose linear row is all zeros (text, or a block with no
+  // linear keys) would otherwise scale 0 by 1/sqrt(0)
+  if (!std::isfinite(eps) || !(eps > 0.f)) return fail(VDN_ERR_INVALID_ARG, "eps must be finite and > 0");
   const void* need_ptr[] = {soft_out, lin_out, gate_lin, norm_weight, out};
   for (const void* x : need_ptr)
     if (x == nullptr)

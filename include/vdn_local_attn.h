@@ -58,7 +58,10 @@ typedef enum {
   VDN_ERR_ALIGNMENT = -3,   /* q/k/v/out not 16-byte aligned, gate/lse/scales
                                not 4-byte aligned                               */
   VDN_ERR_OVERFLOW = -4,    /* S or a tensor's element count does not fit the
-                               kernel's index types                             */
+                               kernel's index types, or 128 token strides
+                               (128 * heads * head_dim * element bytes) reach
+                               2^32 bytes (the tiled kernels' 32-bit per-lane
+                               DMA offsets)                                     */
   VDN_ERR_HIP = -5,         /* a HIP runtime call failed (message has details) */
   VDN_ERR_CAPACITY = -6     /* a host output array is too small                 */
 } vdn_status_t;
@@ -198,7 +201,8 @@ int64_t vdn_linear_branch_workspace_bytes(int F, int tokens_per_frame,
  *                      the soft_out buffer itself, otherwise must not overlap
  *                      an input.
  *   head_dim           a multiple of 8; heads * head_dim <= 8192.
- *   eps                finite, >= 0.
+ *   eps                finite, > 0 (a token whose linear row is all zeros
+ *                      then gets a linear term of exactly 0).
  * bf16 buffers and norm_weight 16-byte aligned, gate_lin 4-byte aligned.
  * tokens == 0 is a no-op.  No allocation, no synchronisation.
  */
@@ -227,7 +231,7 @@ int vdn_hybrid_fuse(const void* soft_out, const void* lin_out,
  *            lse may be NULL).
  *   gate_lin device fp32 [batch, S, heads] logits of the linear branch's gate.
  *   norm_weight device fp32 [heads * head_dim], 16-byte aligned.
- *   eps      finite, >= 0.
+ *   eps      finite, > 0 (an all-zero linear row then contributes exactly 0).
  *   out      device, [batch, S, heads, head_dim] bfloat16.
  *   workspace device, caller-owned, at least vdn_hybrid_attn_workspace_bytes
  *            bytes, 256-byte aligned; holds the linear branch's states, its

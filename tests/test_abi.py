@@ -156,12 +156,52 @@ ERROR_CASES = [
     ("lse aliases gate", dict(lse=A + 3 * STEP), -1),
     ("lse inside out", dict(lse=A + 4 * STEP + 64), -1),
     ("too many query blocks", dict(F=400, T=4, N=0, Bf=1), -2),
+    # 128 token strides of heads * head_dim elements reach 2^32 bytes: the
+    # kernels' 32-bit per-lane DMA offsets would wrap (tensors of ~200 MB)
+    ("DMA offsets wrap bf16", dict(F=1, T=6, N=0, Bf=1, H=1 << 17), -4),
+    ("DMA offsets wrap fp8", dict(F=1, T=6, N=0, Bf=1, H=1 << 18, dtype=1, scales=A + 6 * STEP), -4),
 ]
 
 
 @pytest.mark.parametrize("name,kw,code", ERROR_CASES, ids=[c[0] for c in ERROR_CASES])
 def test_forward_argument_errors(L, name, kw, code):
     rc = call(L, fwd_args(**kw))
+    assert rc == code, (name, rc, B.vdn_last_error())
+    assert B.vdn_last_error() != ""
+
+
+def bwd_args(**kw):
+    args = dict(q=A, k=A + STEP, v=A + 2 * STEP, gate=A + 3 * STEP, out=A + 4 * STEP, dout=A + 5 * STEP,
+                lse=A + 6 * STEP, dq=A + 7 * STEP, dk=A + 8 * STEP, dv=A + 9 * STEP, dgate=A + 10 * STEP,
+                F=20, T=1008, N=512, Bf=5, H=32, D=128, batch=1, sm=0.0, ws=A + 11 * STEP, stream=None)
+    args.update(kw)
+    return args
+
+
+BWD_ERRORS = [
+    ("F=0", dict(F=0), -1),
+    ("heads=0", dict(H=0), -1),
+    ("dq NULL", dict(dq=None), -1),
+    ("workspace NULL", dict(ws=None), -1),
+    ("dgate without gate", dict(gate=None), -1),
+    ("gate without dgate", dict(dgate=None), -1),
+    ("head_dim 96", dict(D=96), -2),
+    ("scale nan", dict(sm=float("nan")), -1),
+    ("dk misaligned", dict(dk=A + 8 * STEP + 8), -3),
+    ("workspace misaligned", dict(ws=A + 11 * STEP + 2), -3),
+    ("S overflow", dict(F=1 << 20, T=1 << 11), -4),
+    ("DMA offsets wrap", dict(F=1, T=6, N=0, Bf=1, H=1 << 17), -4),
+    ("dv aliases v", dict(dv=A + 2 * STEP), -1),
+    ("workspace inside dq", dict(ws=A + 7 * STEP + 4096), -1),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BWD_ERRORS, ids=[c[0] for c in BWD_ERRORS])
+def test_backward_argument_errors(L, name, kw, code):
+    a = bwd_args(**kw)
+    rc = L.vdn_local_attn_bwd(a["q"], a["k"], a["v"], a["gate"], a["out"], a["dout"], a["lse"], a["dq"],
+                              a["dk"], a["dv"], a["dgate"], a["F"], a["T"], a["N"], a["Bf"], a["H"],
+                              a["D"], a["batch"], a["sm"], a["ws"], a["stream"])
     assert rc == code, (name, rc, B.vdn_last_error())
     assert B.vdn_last_error() != ""
 
@@ -249,6 +289,7 @@ FUSE_ERRORS = [
     ("too wide", dict(H=128, D=128), -2),
     ("eps nan", dict(eps=float("nan")), -1),
     ("eps<0", dict(eps=-1.0), -1),
+    ("eps=0", dict(eps=0.0), -1),
     ("gate NULL", dict(gate=None), -1),
     ("weight NULL", dict(w=None), -1),
     ("soft misaligned", dict(soft=A + 8), -3),
@@ -305,6 +346,7 @@ HYB_ERRORS = [
     ("norm_weight NULL", dict(w=None), -1),
     ("workspace NULL", dict(ws=None), -1),
     ("eps negative", dict(eps=-1.0), -1),
+    ("eps zero", dict(eps=0.0), -1),
     ("eps NaN", dict(eps=float("nan")), -1),
     ("workspace small", dict(ws_bytes=1 << 20), -1),
     ("workspace misaligned", dict(ws=A + 8 * STEP + 64), -3),
