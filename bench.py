@@ -6,9 +6,12 @@ inputs already resident in HBM.  Prints one JSON line with effective TFLOP/s
 (allowed (query, key) pairs only: 4*D flops per pair per head), ms per step,
 the fraction of the dense MFMA peak, the speedup over the same kernel run
 dense (block_frames = F), and the CPU oracle timed on a bounded sample.
-Extra workloads (the fp8 forward, the backward pass, the complement linear
-branch, the two-branch fusion and the whole hybrid attention output) are
-reported under "other_workloads".
+Every timed line also carries the median of its per-call durations (one HIP
+event before each call on the launch stream).  Extra workloads -- the medium,
+long-video and fp8 forward configurations (each with its dense run and a CPU
+oracle sample), the backward pass, the complement linear branch, the
+two-branch fusion, the whole hybrid attention output and one GPU's 4-head
+share -- are reported under "other_workloads".
 
     python bench.py [--steps K] [--warmup W] [--workload 768p]
 """
@@ -32,7 +35,8 @@ PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 KERNEL_SOURCES = {"bf16": ["fwd_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"],
                   "fp8": ["fwd_fp8_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"],
-                  "linear": ["linear_kernel.hip", "linear_params.hpp", "fwd_common.hpp"]}
+                  "linear": ["linear_kernel.hip", "linear_params.hpp", "fwd_common.hpp"],
+                  "bwd": ["bwd_kernel.hip", "fwd_common.hpp", "fwd_params.hpp"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{kernel}_{workload}.json")
 
 
@@ -59,6 +63,25 @@ def load_traffic(dtype: str, workload: str, kernel: str | None = None):
     if rec.get("kernel_source_sha256_16") != kernel_source_hash(dtype):
         return None
     return rec.get("bytes_per_launch")
+
+
+def host_cpu() -> dict:
+    """The host CPU the oracle runs on: model name, logical CPUs, and the CPUs
+    this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": affinity}
 
 
 def cpu_baseline(w, inp, seconds: float):
@@ -92,10 +115,13 @@ def cpu_baseline(w, inp, seconds: float):
         if t_total >= seconds:
             break
     flops = 4.0 * w.D * allowed * done
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{w.name}: sample 0, {done} of {w.H} heads, all {w.S} query rows "
-                      f"({done * allowed} allowed pairs), fp64 NumPy, {t_total:.1f} s"}
+    rec = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{w.name}: sample 0, {done} of {w.H} heads, all {w.S} query rows "
+                     f"({done * allowed} allowed pairs), fp64 NumPy, {t_total:.1f} s",
+           "ms_per_head": round(1e3 * t_total / done, 1)}
+    rec.update(host_cpu())
+    return rec
 
 
 def main() -> int:
@@ -104,9 +130,12 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="768p")
-    ap.add_argument("--dense-steps", type=int, default=20, help="0 skips the dense run")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="0 skips the CPU baseline")
-    ap.add_argument("--also", default="768p-fp8,768p-bwd,768p-linear,768p-fuse,768p-hybrid,768p-h4",
+    ap.add_argument("--dense-steps", type=int, default=20, help="0 skips the dense runs")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU oracle budget for the headline workload (0 skips every CPU baseline)")
+    ap.add_argument("--cpu-seconds-other", type=float, default=4.0,
+                    help="CPU oracle budget for each other forward configuration")
+    ap.add_argument("--also", default="768p-fp8,medium,long,768p-bwd,768p-linear,768p-fuse,768p-hybrid,768p-h4",
                     help="comma-separated extra workloads reported under 'other_workloads' "
                          "(suffixes: '-bwd' the backward pass, '-linear' the linear branch, "
                          "'-fuse' the fusion, '-hybrid' softmax + linear + fusion; '' for none)")
@@ -129,6 +158,7 @@ def main() -> int:
     binding.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    other_steps = max(args.steps, 20)
 
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib << 20
@@ -138,7 +168,33 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    def measure(name: str, steps: int, warmup: int, dense_steps: int):
+    def time_calls(step, steps: int, warmup: int):
+        """(mean ms, median ms, wall ms) per call over `steps` back-to-back
+        calls: an event is recorded on the launch stream before every call and
+        after the last, so the mean is the bracketed total over `steps`."""
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i].record(stream)
+            step()
+        ev[steps].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        mean = ev[0].elapsed_time(ev[steps]) / steps
+        mid = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+        return mean, mid, wall
+
+    def shape_config(w):
+        return {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D, "frames": w.F,
+                "tokens_per_frame": w.T, "text_tokens": w.N, "seq_len": w.S, "block_frames": w.Bf}
+
+    def measure(name: str, steps: int, warmup: int, dense_steps: int, cpu_seconds: float):
+        """The forward pass of a configuration: sparse, dense (block_frames
+        = F) on the same inputs, and the CPU oracle on a bounded sample."""
         w = synth.WORKLOADS[name]
         inp = synth.make_inputs(w)
         q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
@@ -146,51 +202,46 @@ def main() -> int:
         scales = None if inp["scales"] is None else inp["scales"].to(dev)
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
 
-        def step(bf):
-            binding.vdn_local_attn_fwd(q, k, v, gate, out, w.F, w.T, w.N, bf, qkv_scales=scales,
-                                       stream=stream.cuda_stream)
+        def run(bf):
+            return lambda: binding.vdn_local_attn_fwd(q, k, v, gate, out, w.F, w.T, w.N, bf, qkv_scales=scales,
+                                                      stream=stream.cuda_stream)
 
-        def timed(bf, n_steps, n_warm):
-            for _ in range(n_warm):
-                step(bf)
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            t0 = time.perf_counter()
-            e0.record(stream)
-            for _ in range(n_steps):
-                step(bf)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / n_steps, (time.perf_counter() - t0) * 1e3 / n_steps
-
-        ms, wall_ms = timed(w.Bf, steps, warmup)
-        print(f"[bench] {w.name} sparse: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
-        dense_ms = None
+        ms, med, wall_ms = time_calls(run(w.Bf), steps, warmup)
+        print(f"[bench] {w.name} sparse: {ms:.4f} ms/step (median {med:.4f}) over {steps} steps",
+              file=sys.stderr, flush=True)
+        dense_ms = dense_med = None
         if dense_steps > 0:
-            dense_ms, _ = timed(w.F, dense_steps, 2)
-            print(f"[bench] {w.name} dense: {dense_ms:.4f} ms/step", file=sys.stderr, flush=True)
+            dense_ms, dense_med, _ = time_calls(run(w.F), dense_steps, 2)
+            print(f"[bench] {w.name} dense: {dense_ms:.4f} ms/step (median {dense_med:.4f})",
+                  file=sys.stderr, flush=True)
         # closed-form count of attended (query, key) pairs, from the library
         allowed, _ = binding.vdn_local_attn_count_pairs(w.F, w.T, w.N, w.Bf)
-        tflops = 4.0 * w.D * w.H * w.B * allowed / (ms * 1e-3) / 1e12
+        flop = 4.0 * w.D * w.H * w.B * allowed
+        tflops = flop / (ms * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.dtype]
+        cfg = shape_config(w)
+        cfg.update({"gate": w.gate, "allowed_pairs_per_head": allowed, "outlier_frac": w.outlier_frac})
         rec = {
             "ms_per_step": round(ms, 4),
+            "ms_per_call_median": round(med, 4),
             "tflops": round(tflops, 2),
+            "tflops_at_median": round(flop / (med * 1e-3) / 1e12, 2),
             "wall_ms_per_step": round(wall_ms, 4),
+            "steps": steps,
             "dtype": w.dtype,
-            "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
-                       "frames": w.F, "tokens_per_frame": w.T, "text_tokens": w.N,
-                       "seq_len": w.S, "block_frames": w.Bf, "gate": w.gate,
-                       "allowed_pairs_per_head": allowed},
+            "config": cfg,
             "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
             "dense_ms_per_step": None if dense_ms is None else round(dense_ms, 4),
+            "dense_ms_per_call_median": None if dense_med is None else round(dense_med, 4),
             "sparse_vs_dense_speedup": None if dense_ms is None else round(dense_ms / ms, 3),
+            "ideal_sparse_vs_dense_speedup": round(float(w.S) * w.S / allowed, 3),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                          "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                          "traffic": load_traffic(w.dtype, w.name)},
         }
-        return w, inp, rec
+        if cpu_seconds > 0:
+            rec["cpu_baseline"] = cpu_baseline(w, inp, cpu_seconds)
+        return rec
 
     def measure_bwd(name: str, steps: int, warmup: int):
         """The backward pass of a workload (inputs, upstream gradient, and the
@@ -209,49 +260,23 @@ def main() -> int:
         def step():
             binding.vdn_local_attn_bwd(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, w.F, w.T, w.N,
                                        w.Bf, workspace=ws, stream=stream.cuda_stream)
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        print(f"[bench] {w.name} backward: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
+        ms, med, _ = time_calls(step, steps, warmup)
+        print(f"[bench] {w.name} backward: {ms:.4f} ms/step (median {med:.4f}) over {steps} steps",
+              file=sys.stderr, flush=True)
         allowed, _ = binding.vdn_local_attn_count_pairs(w.F, w.T, w.N, w.Bf)
         # 2.5x the forward's work: S recomputed, dP, dS K, dS^T Q, P^T dO
         tflops = 10.0 * w.D * w.H * w.B * allowed / (ms * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.dtype]
-        return {"ms_per_step": round(ms, 4), "tflops": round(tflops, 2), "dtype": w.dtype,
-                "pass": "backward (dq, dk, dv, dgate)",
+        cfg = shape_config(w)
+        cfg["gate"] = w.gate
+        return {"ms_per_step": round(ms, 4), "ms_per_call_median": round(med, 4), "tflops": round(tflops, 2),
+                "steps": steps, "dtype": w.dtype, "pass": "backward (dq, dk, dv, dgate)",
                 "flop_convention": "10*D per attended pair per head (2.5x forward)",
-                "config": {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D,
-                           "frames": w.F, "tokens_per_frame": w.T, "text_tokens": w.N,
-                           "seq_len": w.S, "block_frames": w.Bf, "gate": w.gate},
+                "config": cfg,
                 "pct_of_mfma_peak": round(100.0 * tflops / peak, 2),
                 "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                             "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None}}
-
-    def event_time(step, steps: int, warmup: int) -> float:
-        """Average ms per step between two events on the launch stream."""
-        for _ in range(warmup):
-            step()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    def shape_config(w):
-        return {"workload": w.name, "batch": w.B, "heads": w.H, "head_dim": w.D, "frames": w.F,
-                "tokens_per_frame": w.T, "text_tokens": w.N, "seq_len": w.S, "block_frames": w.Bf}
+                             "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                             "traffic": load_traffic("bwd", w.name, "bwd")}}
 
     def linear_bytes(w) -> int:
         """Compulsory HBM bytes of the linear branch: K and V of frames
@@ -283,11 +308,12 @@ def main() -> int:
         def step():
             binding.vdn_linear_branch_fwd(q, k, v, out, w.F, w.T, w.N, w.Bf, workspace=ws,
                                           stream=stream.cuda_stream)
-        ms = event_time(step, steps, warmup)
-        print(f"[bench] {w.name} linear branch: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
+        ms, med, _ = time_calls(step, steps, warmup)
+        print(f"[bench] {w.name} linear branch: {ms:.4f} ms/step (median {med:.4f}) over {steps} steps",
+              file=sys.stderr, flush=True)
         nbytes = linear_bytes(w)
-        return {"ms_per_step": round(ms, 4), "dtype": "bf16",
-                "pass": "complement linear branch (frame states, block states, apply)",
+        return {"ms_per_step": round(ms, 4), "ms_per_call_median": round(med, 4), "steps": steps,
+                "dtype": "bf16", "pass": "complement linear branch (frame states, block states, apply)",
                 "algorithmic_bytes": nbytes, "workspace_bytes": nws,
                 "config": shape_config(w),
                 "roofline": hbm_roofline(nbytes, ms, load_traffic("linear", w.name, "linear"))}
@@ -302,12 +328,13 @@ def main() -> int:
 
         def step():
             binding.vdn_hybrid_fuse(soft, lin, gate, weight, out, 1e-6, stream=stream.cuda_stream)
-        ms = event_time(step, steps, warmup)
-        print(f"[bench] {w.name} fusion: {ms:.4f} ms/step over {steps} steps", file=sys.stderr, flush=True)
+        ms, med, _ = time_calls(step, steps, warmup)
+        print(f"[bench] {w.name} fusion: {ms:.4f} ms/step (median {med:.4f}) over {steps} steps",
+              file=sys.stderr, flush=True)
         tokens = w.B * w.S
         nbytes = 3 * tokens * w.H * w.D * 2 + tokens * w.H * 4 + w.H * w.D * 4
-        return {"ms_per_step": round(ms, 4), "dtype": "bf16",
-                "pass": "fusion: soft + sigmoid(g) * RMSNorm(lin) * w",
+        return {"ms_per_step": round(ms, 4), "ms_per_call_median": round(med, 4), "steps": steps,
+                "dtype": "bf16", "pass": "fusion: soft + sigmoid(g) * RMSNorm(lin) * w",
                 "algorithmic_bytes": nbytes, "config": shape_config(w),
                 "roofline": hbm_roofline(nbytes, ms, load_traffic("linear", w.name, "fuse"))}
 
@@ -329,8 +356,8 @@ def main() -> int:
             binding.vdn_local_attn_fwd(q, k, v, gate, soft, w.F, w.T, w.N, w.Bf, stream=st)
             binding.vdn_linear_branch_fwd(q, k, v, lin, w.F, w.T, w.N, w.Bf, workspace=ws, stream=st)
             binding.vdn_hybrid_fuse(soft, lin, gl, weight, soft, 1e-6, stream=st)
-        ms = event_time(step, steps, warmup)
-        print(f"[bench] {w.name} hybrid layer attention, three calls: {ms:.4f} ms/step over {steps} steps",
+        ms, med, _ = time_calls(step, steps, warmup)
+        print(f"[bench] {w.name} hybrid layer attention, three calls: {ms:.4f} ms/step (median {med:.4f})",
               file=sys.stderr, flush=True)
         # one call: the linear branch, then the softmax branch with the fusion
         # in its epilogue
@@ -340,10 +367,11 @@ def main() -> int:
         def step1():
             binding.vdn_hybrid_attn_fwd(q, k, v, gate, gl, weight, soft, w.F, w.T, w.N, w.Bf,
                                         eps=1e-6, workspace=ws1, stream=st)
-        ms1 = event_time(step1, steps, warmup)
-        print(f"[bench] {w.name} hybrid layer attention, one call: {ms1:.4f} ms/step over {steps} steps",
+        ms1, med1, _ = time_calls(step1, steps, warmup)
+        print(f"[bench] {w.name} hybrid layer attention, one call: {ms1:.4f} ms/step (median {med1:.4f})",
               file=sys.stderr, flush=True)
-        return {"ms_per_step": round(ms1, 4), "ms_per_step_three_calls": round(ms, 4), "dtype": "bf16",
+        return {"ms_per_step": round(ms1, 4), "ms_per_call_median": round(med1, 4),
+                "ms_per_step_three_calls": round(ms, 4), "steps": steps, "dtype": "bf16",
                 "pass": "hybrid attention output: linear branch, then the softmax branch with the "
                         "fusion in its epilogue (vdn_hybrid_attn_fwd); three_calls: softmax branch, "
                         "linear branch, fusion kernel",
@@ -351,7 +379,7 @@ def main() -> int:
                 "context": "whole-layer figures on the pages (332.5 / 192.1 / 125.3 ms per layer on "
                            "one B200) include projections and other hardware; not a target"}
 
-    w, inp, main_rec = measure(args.workload, args.steps, args.warmup, args.dense_steps)
+    main_rec = measure(args.workload, args.steps, args.warmup, args.dense_steps, args.cpu_seconds)
     result = {
         "metric": METRIC,
         "value": main_rec["tflops"],
@@ -366,29 +394,31 @@ def main() -> int:
         "dtype": main_rec["dtype"],
         "data": "synthetic",
         "config": main_rec["config"],
-        "pct_of_mfma_peak": main_rec["pct_of_mfma_peak"],
-        "wall_ms_per_step": main_rec["wall_ms_per_step"],
-        "dense_ms_per_step": main_rec["dense_ms_per_step"],
-        "sparse_vs_dense_speedup": main_rec["sparse_vs_dense_speedup"],
-        "roofline": main_rec["roofline"],
     }
+    for key in ("ms_per_call_median", "tflops_at_median", "pct_of_mfma_peak", "wall_ms_per_step",
+                "dense_ms_per_step", "dense_ms_per_call_median", "sparse_vs_dense_speedup",
+                "ideal_sparse_vs_dense_speedup", "roofline"):
+        result[key] = main_rec[key]
     others = {}
+    cpu_other = args.cpu_seconds_other if args.cpu_seconds > 0 else 0.0
     for name in [x for x in args.also.split(",") if x and x != args.workload]:
         if name.endswith("-bwd"):
-            others[name] = measure_bwd(name[:-4], max(args.steps // 5, 5), max(args.warmup // 5, 2))
+            others[name] = measure_bwd(name[:-4], other_steps, max(args.warmup // 2, 2))
         elif name.endswith("-linear"):
-            others[name] = measure_linear(name[:-7], args.steps, args.warmup)
+            others[name] = measure_linear(name[:-7], other_steps, args.warmup)
         elif name.endswith("-fuse"):
-            others[name] = measure_fuse(name[:-5], args.steps, args.warmup)
+            others[name] = measure_fuse(name[:-5], other_steps, args.warmup)
         elif name.endswith("-hybrid"):
-            others[name] = measure_hybrid(name[:-7], max(args.steps // 2, 5), max(args.warmup // 2, 2))
+            others[name] = measure_hybrid(name[:-7], other_steps, max(args.warmup // 2, 2))
         else:
-            _, _, rec = measure(name, max(args.steps // 2, 5), max(args.warmup // 2, 2), 0)
-            others[name] = rec
+            dense = args.dense_steps if name != "768p-h4" else 0
+            others[name] = measure(name, other_steps, max(args.warmup // 2, 2), dense,
+                                   cpu_other if name != "768p-h4" else 0.0)
+        torch.cuda.empty_cache()
     if others:
         result["other_workloads"] = others
-    if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    if "cpu_baseline" in main_rec:
+        result["cpu_baseline"] = main_rec["cpu_baseline"]
     print(json.dumps(result), flush=True)
     return 0
 

@@ -46,3 +46,15 @@ def test_stale_traffic_record_is_not_reported(monkeypatch):
     for dtype, workload, kernel in RECORDS:
         assert bench.load_traffic(dtype, workload, kernel) is None
     assert bench.load_traffic("bf16", "no-such-workload") is None
+
+
+def test_host_cpu_record():
+    rec = bench.host_cpu()
+    assert rec["nproc"] == os.cpu_count()
+    assert 1 <= rec["affinity"] <= rec["nproc"]
+    assert rec["cpu_model"] is None or isinstance(rec["cpu_model"], str)
+
+
+def test_every_source_set_hashes():
+    for dtype in bench.KERNEL_SOURCES:
+        assert len(bench.kernel_source_hash(dtype)) == 16

@@ -231,6 +231,13 @@ def test_bad_arguments_raise_without_launch():
 # near that figure; the bar leaves a 2.5x margin.  Max-abs uses the 6e-2 bar
 # for ~N(0,1) inputs.
 FP8_REL_L2 = 0.1
+# At the full 768p shape each row sums thousands of rounded weights, whose
+# errors average out: the relative L2 error measured on sampled rows of three
+# heads was 0.0077-0.0093 across boxes and kernel versions (running maximum
+# lagging by 0 to 2).  The bar for the full-shape case is ~2.7x that figure,
+# so a systematic error of a few percent (a wrong scale, P requantised
+# against the wrong maximum) fails it.
+FP8_REL_L2_768P = 0.025
 # The denominator sums the rounded weights, each within 2^-4 of its exact
 # value, so the log-sum-exp is within ln(1 + 2^-4) of the exact one.
 FP8_LSE_TOL = 0.0607
@@ -267,7 +274,7 @@ def test_fp8_768p_sampled():
     sub = subset_heads(inp, heads)
     orf, lrf = oracle.attend(*oracle_inputs(sub), w.F, w.T, w.N, w.Bf, rows=rows)
     stats = compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows, max_abs=FP8_MAX_ABS,
-                    rel_l2=FP8_REL_L2, lse_tol=FP8_LSE_TOL, v_rms=value_channel_rms(sub))
+                    rel_l2=FP8_REL_L2_768P, lse_tol=FP8_LSE_TOL, v_rms=value_channel_rms(sub))
     _log("768p-fp8", stats)
     # the plain max-abs bar, unnormalised, on the channels drawn N(0, 1)
     plain = value_channel_rms(sub) < 2.0

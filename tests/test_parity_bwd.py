@@ -190,3 +190,21 @@ def test_768p_sampled():
     sel = np.ix_(range(w.B), rows, heads)
     check("768p sampled dq/dgate", [dq[sel], None, None, dg[sel]],
           [ref[0][sel], None, None, ref[3][sel]])
+
+
+def test_768p_two_heads_full():
+    # the 768p launch (32 heads): every gradient of two heads compared element
+    # by element.  Its 1008-token frames give key groups of 4032, 5040 and
+    # 2528 keys that end inside a dK/dV tile, which the medium workload's
+    # 1024-token frames never reach at full size.
+    w = synth.WORKLOADS["768p"]
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    got = run_bwd(inp, dout, w)
+    heads = [0, 31]
+    idx = torch.tensor(heads)
+    sub = {n: inp[n].index_select(2, idx).contiguous() for n in ("q", "k", "v")}
+    sub["gate"] = inp["gate"].index_select(2, idx).contiguous()
+    sub["scales"] = None
+    ref = _oracle(sub, dout.index_select(2, idx).contiguous(), w)
+    check("768p heads 0,31 (all gradients)", [None if g is None else g[:, :, heads] for g in got], ref)

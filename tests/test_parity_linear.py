@@ -302,3 +302,68 @@ def test_hybrid_one_call(kw):
     check("hybrid one call vs three calls", got, three.cpu().to(torch.float64).numpy())
     # the log-sum-exp output is the softmax branch's
     assert np.max(np.abs(lse.cpu().numpy() - lse_ref)) <= 2e-3
+
+
+def _run_one_call(w, seed_offset_step=0.2):
+    """vdn_hybrid_attn_fwd on a workload's inputs (v with per-frame offsets);
+    returns the GPU output and log-sum-exp and the oracle's fp64 inputs."""
+    inp = synth.make_inputs(w)
+    v = synth.with_frame_offsets(inp["v"], w.F, w.T, seed_offset_step)
+    fi = synth.make_fuse_inputs(w)
+    q, k, vd = (t.to(DEV) for t in (inp["q"], inp["k"], v))
+    g = None if inp["gate"] is None else inp["gate"].to(DEV)
+    n = B.vdn_hybrid_attn_workspace_bytes(w.F, w.T, w.N, w.Bf, w.H, w.D, w.B)
+    ws = torch.full((n,), 255, dtype=torch.uint8, device=DEV)
+    out = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=DEV)
+    B.vdn_hybrid_attn_fwd(q, k, vd, g, fi["gate"].to(DEV), fi["weight"].to(DEV), out, w.F, w.T, w.N, w.Bf,
+                          eps=1e-6, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().to(torch.float64).numpy()
+    del q, k, vd, g, ws, out
+    qn, kn, vn, gn = oracle_inputs({"q": inp["q"], "k": inp["k"], "v": v, "gate": inp["gate"], "scales": None})
+    return got, lse.cpu().numpy(), (qn, kn, vn, gn), fi
+
+
+def test_hybrid_one_call_768p_two_heads_full():
+    # the size the one-call hybrid is benchmarked at: 32 heads (each token's
+    # RMSNorm spans all of them in the fused prologue), whole 256-row tiles
+    # (no half tiles at this size) and the peeled last step of every tile;
+    # two heads compared element by element against attend -> linear_branch
+    # (all 32 heads) -> hybrid_fuse
+    w = synth.WORKLOADS["768p"]
+    got, lse, (qn, kn, vn, gn), fi = _run_one_call(w)
+    heads = [0, 31]
+    soft_ref, lse_ref = oracle.attend(qn, kn, vn, gn, w.F, w.T, w.N, w.Bf, heads=heads)
+    lin_ref = oracle.linear_branch(qn, kn, vn, w.F, w.T, w.N, w.Bf)
+    ref = oracle.hybrid_fuse(soft_ref, lin_ref, fi["gate"].to(torch.float64).numpy(),
+                             fi["weight"].to(torch.float64).numpy(), 1e-6)
+    check("hybrid one call 768p heads 0,31", got[:, :, heads], ref[:, :, heads])
+    assert np.max(np.abs(lse[:, heads] - lse_ref[:, heads])) <= 2e-3
+
+
+def _in_tile_rows(w, tile=256):
+    """Rows at both ends and across the middle of every 256-row tile of every
+    query block (tile offsets 0, 1, 127, 128, 129, 200 and 255)."""
+    rows = set()
+    for lo, hi in oracle.query_blocks(w.F, w.T, w.N, w.Bf):
+        for r0 in range(lo, hi, tile):
+            rows.update(r for r in (r0, r0 + 1, r0 + 127, r0 + 128, r0 + 129, r0 + 200, r0 + 255) if r < hi)
+        rows.update({hi - 2, hi - 1})
+    return np.array(sorted(rows))
+
+
+def test_hybrid_one_call_768p_h4_sampled():
+    # one GPU's share of the 768p heads (4): most tiles run whole and the last
+    # 16 tiles of each XCD share run as 128-row halves, so both the waves
+    # staging rows 128..255 of a whole tile's linear output and the half
+    # tiles are exercised; rows at every in-tile offset class of all 4 heads
+    w = synth.WORKLOADS["768p-h4"]
+    got, lse, (qn, kn, vn, gn), fi = _run_one_call(w)
+    rows = _in_tile_rows(w)
+    soft_ref, lse_ref = oracle.attend(qn, kn, vn, gn, w.F, w.T, w.N, w.Bf, rows=rows)
+    lin_ref = oracle.linear_branch(qn, kn, vn, w.F, w.T, w.N, w.Bf)
+    ref = oracle.hybrid_fuse(soft_ref, lin_ref, fi["gate"].to(torch.float64).numpy(),
+                             fi["weight"].to(torch.float64).numpy(), 1e-6)
+    check(f"hybrid one call 768p-h4, {rows.size} rows", got[:, rows], ref[:, rows])
+    assert np.max(np.abs(lse[:, :, rows] - lse_ref[:, :, rows])) <= 2e-3
