@@ -36,6 +36,7 @@ _pint = ctypes.POINTER(ctypes.c_int)
 SIGNATURES = {
     "vdn_local_attn_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _f, _p, _p]),
     "vdn_local_attn_bwd": (_i, [_p] * 11 + [_i] * 7 + [_f, _p, _p]),
+    "vdn_local_attn_bwd_noalloc": (_i, [_p] * 11 + [_i] * 7 + [_f, _p]),
     "vdn_local_attn_num_query_blocks": (_i, [_i, _i, _i, _i]),
     "vdn_local_attn_key_intervals": (_i, [_i, _i, _i, _i, _pi64, _pi64, _i, _pint]),
     "vdn_local_attn_count_pairs": (_i, [_i, _i, _i, _i, _pi64, _pi64]),
@@ -263,6 +264,35 @@ def vdn_local_attn_bwd(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, F: int,
         _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(out), _ptr(dout), _ptr(lse),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), F, tokens_per_frame, n_text, block_frames,
         H, D, B, float(softmax_scale), _ptr(workspace), ctypes.c_void_p(stream))
+    _check(rc)
+
+
+def vdn_local_attn_bwd_noalloc(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, F: int,
+                               tokens_per_frame: int, n_text: int, block_frames: int = 5,
+                               softmax_scale: float = 0.0, stream=None) -> None:
+    """vdn_local_attn_bwd with the library's fixed per-GPU scratch in place of
+    a workspace (the call allocates nothing); tensors as there."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout),
+                    ("dq", dq), ("dk", dk), ("dv", dv)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must have the shape of q")
+    B, S, H, D = q.shape
+    for name, t, shape in (("gate", gate, (B, S, H)), ("dgate", dgate, (B, S, H)), ("lse", lse, (B, H, S))):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be a contiguous fp32 GPU tensor")
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must have shape {shape}, got {tuple(t.shape)}")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib().vdn_local_attn_bwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(out), _ptr(dout), _ptr(lse),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate), F, tokens_per_frame, n_text, block_frames,
+        H, D, B, float(softmax_scale), ctypes.c_void_p(stream))
     _check(rc)
 
 

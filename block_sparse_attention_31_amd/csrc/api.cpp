@@ -319,18 +319,21 @@ int vdn_local_attn_fwd(const void* q, const void* k, const void* v, const float*
                              nullptr);
 }
 
-int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float* gate,
-                       const void* out, const void* dout, const float* lse, void* dq, void* dk,
-                       void* dv, float* dgate, int F, int tokens_per_frame, int n_text,
-                       int block_frames, int heads, int head_dim, int batch, float softmax_scale,
-                       float* workspace, void* hip_stream) {
+// The backward pass; with `fixed_scratch` the per-row constants go to the
+// library's static device array instead of the caller's workspace.
+static int local_attn_bwd_impl(const void* q, const void* k, const void* v, const float* gate,
+                               const void* out, const void* dout, const float* lse, void* dq,
+                               void* dk, void* dv, float* dgate, int F, int tokens_per_frame,
+                               int n_text, int block_frames, int heads, int head_dim, int batch,
+                               float softmax_scale, float* workspace, bool fixed_scratch,
+                               void* hip_stream) {
   vdn::Geometry g;
   std::string err;
   if (!vdn::make_geometry(F, tokens_per_frame, n_text, block_frames, &g, &err))
     return fail(VDN_ERR_INVALID_ARG, err);
   if (heads <= 0 || batch <= 0)
     return fail(VDN_ERR_INVALID_ARG, "heads and batch must be >= 1");
-  const void* need[] = {q, k, v, out, dout, lse, dq, dk, dv, workspace};
+  const void* need[] = {q, k, v, out, dout, lse, dq, dk, dv, fixed_scratch ? q : workspace};
   for (const void* x : need)
     if (x == nullptr)
       return fail(VDN_ERR_INVALID_ARG, "q, k, v, out, dout, lse, dq, dk, dv and workspace must be non-NULL");
@@ -355,12 +358,18 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
   if (!dma_offsets_fit(heads, head_dim, 2))
     return fail(VDN_ERR_OVERFLOW, "128 token strides of heads * head_dim elements exceed 2^32 bytes");
 
+  if (fixed_scratch && 2 * int64_t(batch) * heads * g.S > vdn::kBwdScratchFloats)
+    return fail(VDN_ERR_CAPACITY, "batch * heads * S = " + std::to_string(int64_t(batch) * heads * g.S) +
+                                      " rows exceed the fixed scratch's " +
+                                      std::to_string(vdn::kBwdScratchFloats / 2));
+
   const size_t t_bytes = size_t(elems) * 2u;
   const size_t row_bytes = size_t(batch) * size_t(g.S) * size_t(heads) * 4u;
   const void* ins[] = {q, k, v, out, dout, lse, gate};
   const size_t in_sz[] = {t_bytes, t_bytes, t_bytes, t_bytes, t_bytes, row_bytes, gate ? row_bytes : 0u};
   const void* outs[] = {dq, dk, dv, dgate, workspace};
-  const size_t out_sz[] = {t_bytes, t_bytes, t_bytes, dgate ? row_bytes : 0u, 2 * row_bytes};
+  const size_t out_sz[] = {t_bytes, t_bytes, t_bytes, dgate ? row_bytes : 0u,
+                           fixed_scratch ? 0u : 2 * row_bytes};
   for (int i = 0; i < 5; ++i) {
     for (int j = 0; j < 7; ++j)
       if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j]))
@@ -387,8 +396,8 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
   a.dout = dout;
   a.gate = gate;
   a.lse = lse;
-  a.dw = workspace;
-  a.lw = workspace + size_t(batch) * size_t(heads) * size_t(g.S);
+  a.dw = workspace;  // (the fixed scratch's address is filled in after validation)
+  a.lw = workspace != nullptr ? workspace + size_t(batch) * size_t(heads) * size_t(g.S) : nullptr;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
@@ -461,10 +470,40 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float*
   kv_p.total_tiles = prefix * batch * heads;
   set_dispatch(kv_p);
 
+  if (fixed_scratch) {
+    float* ws = nullptr;
+    const int se = vdn::bwd_scratch(&ws);
+    if (se != 0)
+      return fail(VDN_ERR_HIP, std::string("fixed scratch address: ") + hipGetErrorString(hipError_t(se)));
+    for (vdn::BwdArgs* x : {&dq_p.a, &kv_p.a}) {
+      x->dw = ws;
+      x->lw = ws + size_t(batch) * size_t(heads) * size_t(g.S);
+    }
+  }
   const int rc = vdn::launch_bwd(dq_p, kv_p, head_dim, hip_stream);
   if (rc != 0)
     return fail(VDN_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(hipError_t(rc)));
   return ok();
+}
+
+int vdn_local_attn_bwd(const void* q, const void* k, const void* v, const float* gate,
+                       const void* out, const void* dout, const float* lse, void* dq, void* dk,
+                       void* dv, float* dgate, int F, int tokens_per_frame, int n_text,
+                       int block_frames, int heads, int head_dim, int batch, float softmax_scale,
+                       float* workspace, void* hip_stream) {
+  return local_attn_bwd_impl(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, F, tokens_per_frame,
+                             n_text, block_frames, heads, head_dim, batch, softmax_scale, workspace,
+                             false, hip_stream);
+}
+
+int vdn_local_attn_bwd_noalloc(const void* q, const void* k, const void* v, const float* gate,
+                               const void* out, const void* dout, const float* lse, void* dq,
+                               void* dk, void* dv, float* dgate, int F, int tokens_per_frame,
+                               int n_text, int block_frames, int heads, int head_dim, int batch,
+                               float softmax_scale, void* hip_stream) {
+  return local_attn_bwd_impl(q, k, v, gate, out, dout, lse, dq, dk, dv, dgate, F, tokens_per_frame,
+                             n_text, block_frames, heads, head_dim, batch, softmax_scale, nullptr,
+                             true, hip_stream);
 }
 
 int64_t vdn_linear_branch_workspace_bytes(int F, int tokens_per_frame, int n_text, int block_frames,

@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "fwd_common.hpp"
 
@@ -611,6 +612,34 @@ constexpr int kDqKeys = VDN_DQ_KT;
 constexpr int kDqStages = VDN_DQ_NS;
 constexpr int kKvWaves = 8;
 constexpr int kKvRows128 = VDN_KV_QT;  // query rows per dK/dV step at head_dim 128
+
+// ---- fixed scratch for callers that cannot allocate
+// The per-row constants (lw, dw) of vdn_local_attn_bwd_noalloc live in this
+// file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it only stands in for the symbol): it takes the array's
+// address on the current device from hipGetSymbolAddress, once per device.
+namespace {
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+std::mutex g_scratch_mu;
+float* g_scratch_addr[kMaxScratchDevices] = {};
+}  // namespace
+
+int bwd_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return int(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return int(e);
+    g_scratch_addr[dev] = static_cast<float*>(addr);
+  }
+  *ptr = g_scratch_addr[dev];
+  return int(hipSuccess);
+}
 
 int bwd_dq_tile_m() { return 32 * kDqWaves; }
 int bwd_dkv_tile_n() { return 32 * kKvWaves; }

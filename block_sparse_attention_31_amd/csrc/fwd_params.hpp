@@ -117,6 +117,14 @@ int bwd_dkv_tile_n();
 // Enqueues the backward kernels (bf16 only): the per-row pass, dQ, dK/dV.
 int launch_bwd(const BwdDqParams& dq, const BwdKvParams& kv, int head_dim, void* stream);
 
+// Fixed device scratch of the allocation-free backward entry point: room for
+// the per-row constants of batch * heads * S <= kBwdScratchFloats / 2 rows
+// (32 MiB per GPU).  bwd_scratch returns its address on the current device
+// (hipSuccess or the HIP error code).
+constexpr int64_t kBwdScratchFloats = int64_t(8) << 20;
+constexpr int kMaxScratchDevices = 64;
+int bwd_scratch(float** ptr);
+
 // Kernel-variant properties used by the front end.
 int kernel_tile_m(int head_dim, int dtype);
 

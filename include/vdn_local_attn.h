@@ -63,7 +63,8 @@ typedef enum {
                                2^32 bytes (the tiled kernels' 32-bit per-lane
                                DMA offsets)                                     */
   VDN_ERR_HIP = -5,         /* a HIP runtime call failed (message has details) */
-  VDN_ERR_CAPACITY = -6     /* a host output array is too small                 */
+  VDN_ERR_CAPACITY = -6     /* a host output array, or the fixed scratch of
+                               vdn_local_attn_bwd_noalloc, is too small          */
 } vdn_status_t;
 
 /*
@@ -132,6 +133,30 @@ int vdn_local_attn_bwd(const void* q, const void* k, const void* v,
                        float* dgate, int F, int tokens_per_frame, int n_text,
                        int block_frames, int heads, int head_dim, int batch,
                        float softmax_scale, float* workspace, void* hip_stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * backward pass with the per-row constants in a fixed scratch array that the
+ * library holds on each GPU it runs on (32 MiB, kept until the process ends)
+ * instead of a caller workspace.  Arguments, layout, ownership and errors as
+ * for vdn_local_attn_bwd without `workspace`, plus:
+ *   - batch * heads * S above 4194304 rows returns VDN_ERR_CAPACITY before
+ *     any HIP call;
+ *   - the call allocates nothing and calls no allocating routine; on its
+ *     first use on a device it looks up the array's address there
+ *     (hipGetSymbolAddress; a failure returns VDN_ERR_HIP);
+ *   - every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (different streams, or threads) race and must be
+ *     serialised by the caller.  Nothing in the array needs clearing: the
+ *     first kernel of the pass writes every row it later reads.
+ */
+int vdn_local_attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                               const float* gate, const void* out, const void* dout,
+                               const float* lse, void* dq, void* dk, void* dv,
+                               float* dgate, int F, int tokens_per_frame, int n_text,
+                               int block_frames, int heads, int head_dim, int batch,
+                               float softmax_scale, void* hip_stream);
 
 /*
  * Complement linear branch, forward (bf16), asynchronous on `hip_stream`.

@@ -206,6 +206,22 @@ def test_backward_argument_errors(L, name, kw, code):
     assert B.vdn_last_error() != ""
 
 
+def test_noalloc_backward_capacity_error(L):
+    # batch * heads * S above the fixed scratch's 4194304 rows: rejected
+    # before any HIP call
+    a = bwd_args(batch=7)
+    rc = L.vdn_local_attn_bwd_noalloc(a["q"], a["k"], a["v"], a["gate"], a["out"], a["dout"], a["lse"],
+                                      a["dq"], a["dk"], a["dv"], a["dgate"], a["F"], a["T"], a["N"],
+                                      a["Bf"], a["H"], a["D"], a["batch"], a["sm"], a["stream"])
+    assert rc == -6, B.vdn_last_error()
+    assert "scratch" in B.vdn_last_error()
+    a = bwd_args(dq=None)
+    rc = L.vdn_local_attn_bwd_noalloc(a["q"], a["k"], a["v"], a["gate"], a["out"], a["dout"], a["lse"],
+                                      a["dq"], a["dk"], a["dv"], a["dgate"], a["F"], a["T"], a["N"],
+                                      a["Bf"], a["H"], a["D"], a["batch"], a["sm"], a["stream"])
+    assert rc == -1
+
+
 def test_host_function_errors(L):
     with pytest.raises(B.VdnError) as e:
         B.vdn_local_attn_key_intervals(0, 4, 0, 5)
