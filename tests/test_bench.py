@@ -15,7 +15,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 RECORDS = [("bf16", "768p", None), ("fp8", "768p-fp8", None), ("linear", "768p", "linear"),
-           ("linear", "768p", "fuse")]
+           ("linear", "768p", "fuse"), ("bwd", "768p", "bwd")]
 
 
 def test_more_than_one_gpu_exits_with_a_message():
