@@ -130,6 +130,44 @@ __device__ __forceinline__ TileSlot tile_slot(int w, int per_xcd, int split) {
   return {x * per_xcd + whole + (hs >> 1), 1 + (hs & 1)};
 }
 
+// Persistent launch: each XCD's share of the tile slots is a queue whose
+// positions are claimed with one atomic add on its counter (a workgroup's
+// first slot is its own block index, so the counters count from queue_wg).
+// Claims need only be distinct: relaxed device-scope atomics.
+__device__ __forceinline__ int queue_claim(int* queue, int q) {
+  return __hip_atomic_fetch_add(queue + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The claim on the home queue (block index % 8) for the tile after the
+// current one, taken by thread 0 while the current tile runs.
+struct PendingClaim {
+  int raw = 0;          // thread 0: the home counter's value before the add
+  bool issued = false;  // wave-uniform
+  __device__ __forceinline__ void issue(int* queue, int tid) {
+    if (queue == nullptr || issued) return;
+    issued = true;
+    if (tid == 0) raw = queue_claim(queue, int(blockIdx.x & 7));
+  }
+};
+// Thread 0: the next slot (queue + 8 * position), or -1 once every queue is
+// empty.  `steal` is the next other queue to try (home + steal) % 8.  The
+// workgroup that finds all queues empty last clears the counters for the
+// next launch that uses them.
+__device__ __forceinline__ int next_slot(int* queue, const PendingClaim& c, int qlen, int queue_wg, int& steal) {
+  const int home = int(blockIdx.x & 7);
+  int pos = (c.issued ? c.raw : queue_claim(queue, home)) + queue_wg;
+  if (pos < qlen) return pos * 8 + home;
+  for (; steal < 8; ++steal) {
+    const int y = (home + steal) & 7;
+    pos = queue_claim(queue, y) + queue_wg;
+    if (pos < qlen) return pos * 8 + y;
+  }
+  if (queue_claim(queue, 8) == int(gridDim.x) - 1) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) __hip_atomic_store(queue + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return -1;
+}
+
 // Sets the scores of keys past the end of the key list to -inf on a partial
 // last step.  Score register (kb, r) of a 32x32 MFMA result holds key
 // 32 kb + 8 (r / 4) + 4 (lane / 32) + r % 4 of the step, so in each lane the

@@ -32,12 +32,19 @@
 // RMSNorm and gate); its rows come into LDS with the last step.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "fwd_common.hpp"
 
 #ifndef VDN_PIN_QK
 #define VDN_PIN_QK 1
+#endif
+// persistent workgroups take tiles from other XCDs' queues once their own is
+// empty (1) or stop there (0)
+#ifndef VDN_STEAL
+#define VDN_STEAL 1
 #endif
 // row sums by bf16 dot products over the rounded weights (1) or fp32 adds (0)
 #ifndef VDN_ROWSUM_DOT
@@ -102,14 +109,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     return st == 0 ? Vs0 : st == 1 ? Vs1 : st == 2 ? Vs2 : Vs3;
   };
 
+  __shared__ int redo;    // the workgroup's vote for an online-maximum rerun
+  __shared__ int s_next;  // the next tile's slot, handed from wave 0 to the others
+
+  // One query tile, given its slot in the XCD queues (slot w: queue w % 8,
+  // position w / 8).  `claim` is the pending claim on the home queue, issued
+  // once the tile's first DMA has landed so that its latency hides under the
+  // first step.
+  auto run_tile = [&](const int wslot, PendingClaim& claim) __attribute__((always_inline)) {
   // ---- which tile (XCD-aware, the last tiles of each XCD in halves)
-  const TileSlot slot = tile_slot(blockIdx.x, p.per_xcd, p.split_tail);
+  const TileSlot slot = tile_slot(wslot, p.per_xcd, p.split_tail);
   const int t = slot.tile;
   if (t >= p.total_tiles) return;
-  const int bh = t / p.tiles_per_bh;
-  const int rank = undeal(t - bh * p.tiles_per_bh, p.tiles_per_bh, p.deal);
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
+  // (divisors opaque per tile: their reciprocals are then formed here, not
+  // hoisted out of the tile loop and held in registers across every step)
+  int tpb = p.tiles_per_bh, deal = p.deal, nh = p.H;
+  asm volatile("" : "+s"(tpb), "+s"(deal), "+s"(nh));
+  const int bh = t / tpb;
+  const int rank = undeal(t - bh * tpb, tpb, deal);
+  const int b = bh / nh;
+  const int h = bh - b * nh;
   int bi = 0;
   while (bi + 1 < p.n_qblocks && p.blk[bi + 1].tile_prefix <= rank) ++bi;
   // The block's descriptor, copied once into wave-uniform registers (reading
@@ -215,10 +234,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
         base += step_b;
       }
     } else {
+      // (chunk offset opaque here: its per-instruction 64-bit forms are then
+      // formed on this rare path, not held in registers across the loop)
+      uint32_t ch0 = chunk0;
+      asm volatile("" : "+v"(ch0));
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int j = min(j0 + r0 + i * RPI, n_keys - 1);
-        lds_dma16(gbase + int64_t(vtoken(kl, j)) * rsb + (is_k ? chunk0 ^ kx(i) : chunk0),
+        lds_dma16(gbase + int64_t(vtoken(kl, j)) * rsb + (is_k ? ch0 ^ kx(i) : ch0),
                   lbase + wdst + i * 1024);
       }
     }
@@ -406,6 +429,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       issue(step + NS - 1, kstage(IC<(st + NS - 1) % NS>{}), IC<1>{});
       issue(step + NS - 1, vstage(IC<(st + NS - 1) % NS>{}), IC<0>{});
     }
+    // The claim on the next tile goes out with the tile's last step (the one
+    // that may be partial; the first such step once, so a rerun or the
+    // online loop claims early): tiles are then handed out in the order their
+    // workgroups finish, and the end-of-step wait covers the atomic.
+    if constexpr (!FUSE && decltype(tail_c)::value != 0) claim.issue(p.queue, tid);
     if (active) {
       f32x16 s[NKB];
       qk(kstage(stage_c), s);
@@ -478,7 +506,6 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // rounding unless a later key exceeds the point by so much that a weight
   // overflows: a row sum above 2^32 (no weight above it, no sum near the
   // fp32 range) sends the workgroup through the key list again.
-  __shared__ int redo;
   auto vote_redo = [&]() __attribute__((always_inline)) {
     const float l_chk = xhalf_sum(l_run);
     const bool bad = wave * QW + lr < rows && !(l_chk <= 0x1p32f);
@@ -527,8 +554,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA outlives the workgroup
 
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
+  // (lane-derived offsets re-formed here from an opaque thread index, so
+  // that they are not hoisted out of the tile loop and held across the steps)
+  int etid = threadIdx.x;
+  asm volatile("" : "+v"(etid));
+  const int lr_e = etid & 31, hh_e = (etid >> 5) & 1;
   __bf16* og = static_cast<__bf16*>(p.out) + bh_off;
-  const int lrow = wave * QW + lr;
+  const int lrow = wave * QW + lr_e;
   const float l_tot = xhalf_sum(l_run);
   if (lrow < rows) {
     const int row = row0 + lrow;
@@ -546,7 +578,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
           bf16x4 o4;
 #pragma unroll
           for (int r = 0; r < 4; ++r) o4[r] = static_cast<__bf16>(acc[db][g4 * 4 + r] * scale);
-          *reinterpret_cast<bf16x4*>(dst + db * 32 + g4 * 8 + hh * 4) = o4;
+          *reinterpret_cast<bf16x4*>(dst + db * 32 + g4 * 8 + hh_e * 4) = o4;
         }
       }
     } else {
@@ -556,15 +588,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       const float coef = lin_coef;
       // the row landed in LDS with the last step (stage (nsteps - 1 + NS - 1)
       // % NS, the one the last step did not read)
-      const char* lrow_lds = ((nsteps - 1) % NS == 0 ? lin_stage(IC<1 % NS>{}) : lin_stage(IC<0>{})) + lr * RB;
+      const char* lrow_lds = ((nsteps - 1) % NS == 0 ? lin_stage(IC<1 % NS>{}) : lin_stage(IC<0>{})) + lr_e * RB;
       const float* wsrc = p.lin_w + h * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = db * 32 + g4 * 8 + hh * 4;
-          const int c = (db * 4 + g4) ^ (lr % CH);
-          const bf16x4 l4 = *reinterpret_cast<const bf16x4*>(lrow_lds + c * 16 + hh * 8);
+          const int col = db * 32 + g4 * 8 + hh_e * 4;
+          const int c = (db * 4 + g4) ^ (lr_e % CH);
+          const bf16x4 l4 = *reinterpret_cast<const bf16x4*>(lrow_lds + c * 16 + hh_e * 8);
           const float4 w4 = *reinterpret_cast<const float4*>(wsrc + col);
           const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
           bf16x4 o4;
@@ -575,9 +607,34 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
         }
       }
     }
-    if (p.lse != nullptr && hh == 0) {
+    if (p.lse != nullptr && hh_e == 0) {
       p.lse[(int64_t(b) * p.H + h) * p.S + row] = (m_run + __log2f(l_tot)) * kLn2;
     }
+  }
+  };  // run_tile
+
+  // Each workgroup starts on its own slot.  Persistent (p.queue set), it
+  // then claims slots of its home queue (block index % 8, the XCD it runs
+  // on) and, once that is empty, of the other XCDs' queues; the last one out
+  // resets the counters.  Otherwise that one slot is all.
+  if constexpr (FUSE) {
+    // (the fused instance runs one tile per workgroup: its registers are
+    // already at the limit, and the tile loop's would spill in the steps)
+    PendingClaim none;
+    run_tile(blockIdx.x, none);
+    return;
+  }
+  int wslot = blockIdx.x;
+  int steal = VDN_STEAL ? 1 : 8;  // next queue to try once the home queue is empty
+  for (;;) {
+    PendingClaim claim;
+    run_tile(wslot, claim);
+    if (p.queue == nullptr) break;
+    if (threadIdx.x == 0) s_next = next_slot(p.queue, claim, p.per_xcd + p.split_tail, p.queue_wg, steal);
+    lds_barrier();
+    wslot = __builtin_amdgcn_readfirstlane(s_next);
+    lds_barrier();  // every wave has read the slot before wave 0 writes the next one
+    if (wslot < 0) break;
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -618,26 +675,87 @@ int kernel_tile_m(int head_dim, int dtype) {
   return 32 * kWaves;
 }
 
+namespace {
+// Claim counters of the persistent launches (zero at load; every launch
+// leaves its set zero again).
+__device__ int fwd_queues[kQueueSlots * kQueueInts];
+
+// Per device: the counters' address and, per kernel instance, the
+// workgroups per XCD that fill the device (0: not persistent).
+struct QueueDevice {
+  int* base = nullptr;
+  int wg[2] = {-1, -1};  // [head_dim 64 / 128]
+};
+std::mutex g_queue_mu;
+QueueDevice g_queue_dev[kMaxScratchDevices];
+std::atomic<unsigned> g_queue_seq{0};
+
+// The counter set and workgroups per XCD for one launch of `kernel` (one
+// resident workgroup per CU as its resources allow, the CUs split evenly
+// over the 8 XCDs), or queue = nullptr for a launch of one workgroup per
+// slot.
+int queue_for(const void* kernel, int dim_i, int* wg_per_xcd, int** queue) {
+  *queue = nullptr;
+  *wg_per_xcd = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return 0;
+  std::lock_guard<std::mutex> lock(g_queue_mu);
+  QueueDevice& qd = g_queue_dev[dev];
+  if (qd.base == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(fwd_queues));
+    if (e != hipSuccess) return int(e);
+    qd.base = static_cast<int*>(addr);
+  }
+  int& wg = qd.wg[dim_i];
+  if (wg < 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return int(e);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kWaves, 0);
+    if (e != hipSuccess) return int(e);
+    wg = cus % 8 == 0 ? per_cu * (cus / 8) : 0;
+  }
+  *wg_per_xcd = wg;
+  if (wg > 0) *queue = qd.base + int64_t(g_queue_seq.fetch_add(1) % kQueueSlots) * kQueueInts;
+  return 0;
+}
+
+template <int D, bool FUSE>
+int launch_bf16(const FwdParams& p_in, hipStream_t st) {
+  constexpr int NS = FUSE ? 2 : kStages;
+  const auto kernel = fwd_bf16_kernel<D, kWaves, NS, kKeysPerStep, kReadAhead, kReadAheadV, FUSE, kFixRef>;
+  FwdParams p = p_in;
+  p.queue = nullptr;
+  p.queue_wg = 0;
+  const int slots = p.per_xcd + p.split_tail;  // per XCD queue
+  int wg = 0;
+  int* queue = nullptr;
+  if constexpr (!FUSE) {
+    const int rc = queue_for(reinterpret_cast<const void*>(kernel), D == 128, &wg, &queue);
+    if (rc != 0) return rc;
+  }
+  dim3 grid(unsigned(slots) * 8u);
+  if (!FUSE && queue != nullptr && wg < slots) {
+    p.queue = queue;
+    p.queue_wg = wg;
+    grid = dim3(unsigned(wg) * 8u);
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * kWaves), 0, st, p);
+  return int(hipGetLastError());
+}
+}  // namespace
+
 int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream) {
-  const dim3 grid(unsigned(p.per_xcd + p.split_tail) * 8u);
-  const dim3 block(64 * kWaves);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == 1) return launch_fwd_fp8(p, head_dim, stream);
   if (dtype != 0) return int(hipErrorInvalidValue);
-  if (head_dim == 128) {
-    if (p.lin != nullptr)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true, kFixRef>), grid, block, 0, st, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false, kFixRef>), grid, block, 0, st, p);
-  } else if (head_dim == 64) {
-    if (p.lin != nullptr)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, 2, kKeysPerStep, kReadAhead, kReadAheadV, true, kFixRef>), grid, block, 0, st, p);
-    else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, kWaves, kStages, kKeysPerStep, kReadAhead, kReadAheadV, false, kFixRef>), grid, block, 0, st, p);
-  } else {
-    return int(hipErrorInvalidValue);
-  }
-  return int(hipGetLastError());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool fuse = p.lin != nullptr;
+  if (head_dim == 128) return fuse ? launch_bf16<128, true>(p, st) : launch_bf16<128, false>(p, st);
+  if (head_dim == 64) return fuse ? launch_bf16<64, true>(p, st) : launch_bf16<64, false>(p, st);
+  return int(hipErrorInvalidValue);
 }
 
 }  // namespace vdn

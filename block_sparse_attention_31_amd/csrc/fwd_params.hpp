@@ -54,6 +54,13 @@ struct FwdParams {
   const float* gate_lin;   // [B,S,H] linear-branch gate logits
   const float* lin_w;      // [H*D] RMSNorm weight
   float lin_eps;
+  // Persistent launch (bf16 kernel; nullptr: one workgroup per slot): this
+  // launch's claim counters, kQueueInts ints (one per XCD queue, then the
+  // count of finished workgroups), zero at the start and reset to zero by
+  // the last workgroup; queue_wg workgroups per XCD start on slots 0 ..
+  // queue_wg-1 of their queue and claim the rest.
+  int* queue;
+  int32_t queue_wg;
   QBlockDesc blk[kMaxQueryBlocks];
 };
 
@@ -131,6 +138,11 @@ int kernel_tile_m(int head_dim, int dtype);
 // Enqueues the forward kernel for an already validated FwdParams.  Returns
 // hipSuccess or the HIP error code.
 int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream);
+// Claim counters of the persistent forward launch: kQueueSlots sets of
+// kQueueInts ints in one static device array, handed out round robin (a
+// set is reused only after kQueueSlots further launches in this process).
+constexpr int kQueueInts = 16;
+constexpr int kQueueSlots = 4096;
 
 // fp8 (e4m3) variant, head_dim 128 only.
 int launch_fwd_fp8(const FwdParams& p, int head_dim, void* stream);

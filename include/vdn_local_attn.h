@@ -96,6 +96,15 @@ typedef enum {
  * does not synchronise.  `out` and `lse` must not overlap q, k, v, gate or
  * each other.  Arguments are validated before any HIP call; a launch failure
  * returns VDN_ERR_HIP.
+ *
+ * Shared state: the bf16 kernel runs one resident workgroup per compute
+ * unit, each taking query tiles from per-XCD work queues.  Their claim
+ * counters live in the library's static device memory (no allocation), one
+ * set per launch handed out in rotation from 4096 sets per device and
+ * process, and each launch leaves its set zero when it ends.  So at most 4096
+ * forward launches may be in flight at once per device and process, and a
+ * launch recorded into a HIP graph must not run concurrently with another
+ * replay of itself (replays in stream order are fine).
  */
 int vdn_local_attn_fwd(const void* q, const void* k, const void* v,
                        const float* gate, void* out,
@@ -282,7 +291,9 @@ int64_t vdn_hybrid_attn_workspace_bytes(int F, int tokens_per_frame,
 
 /*
  * Host only.  Number of query blocks for a geometry: ceil(F/block_frames)
- * frame blocks, plus one text block when n_text > 0.  Returns the count
+ * frame blocks, plus one text block when n_text > 0.  The grouping of
+ * latent frames into blocks of consecutive frames is the one of openi.cn
+ * "VDN-MiniMax-H3", technical principles (five frames per block there).  Returns the count
  * (>= 1) or a negative vdn_status_t.
  */
 int vdn_local_attn_num_query_blocks(int F, int tokens_per_frame, int n_text,
@@ -290,7 +301,12 @@ int vdn_local_attn_num_query_blocks(int F, int tokens_per_frame, int n_text,
 
 /*
  * Host only.  The canonical key structure of every query block, in the
- * kernel's block order (frame blocks by index, then text):
+ * kernel's block order (frame blocks by index, then text).  It is the key
+ * set rule at the top of this header written as token intervals (openi.cn
+ * "VDN-MiniMax-H3", technical principles: own block and its neighbours,
+ * first/last-frame anchors; nav.superapi.store, Technical Principles,
+ * "Local Softmax Branch" and "Text Dual-Branch Injection": text keys seen
+ * by every frame):
  *   query_rows    [capacity][2] int64: half-open query token range of each
  *                 block (may be NULL);
  *   key_intervals [capacity][VDN_MAX_KEY_INTERVALS][2] int64: sorted,
@@ -308,6 +324,10 @@ int vdn_local_attn_key_intervals(int F, int tokens_per_frame, int n_text,
  * Host only.  Closed-form counts per (sample, head): *allowed = number of
  * (query, key) pairs attended; *anchor_added = video pairs present only
  * because the key frame is an anchor (frame 0 or F-1) outside the window.
+ * These are the quantities behind the anchors' share of the attended pairs
+ * quoted in nav.superapi.store, Technical Principles, "Local Softmax
+ * Branch", and behind the softmax/linear split of openi.cn "VDN-MiniMax-H3",
+ * technical principles (same key set rule as above).
  */
 int vdn_local_attn_count_pairs(int F, int tokens_per_frame, int n_text,
                                int block_frames, int64_t* allowed,
@@ -315,7 +335,10 @@ int vdn_local_attn_count_pairs(int F, int tokens_per_frame, int n_text,
 
 /*
  * Host only.  The per-(sample, head) query-tile work list (longest key list
- * first; ties by block index, then row): entries [capacity][4] int32 =
+ * first; ties by block index, then row).  The pages define no work
+ * decomposition; each tile's key list is that of its block under the rule
+ * above (openi.cn "VDN-MiniMax-H3", technical principles), and the order is
+ * this implementation's: entries [capacity][4] int32 =
  * {query block, first row, rows, keys}, tiles of `tile_m` rows that never
  * straddle a block boundary.  *n_entries receives the count;
  * VDN_ERR_CAPACITY if capacity is too small.  The kernels concatenate these
@@ -330,8 +353,10 @@ int vdn_local_attn_tile_schedule(int F, int tokens_per_frame, int n_text,
                                  int capacity, int* n_entries);
 
 /*
- * Host only.  The key side of the structure, used by the backward pass: keys
- * grouped by the query rows that see them (frame blocks by index with their
+ * Host only.  The key side of the structure, used by the backward pass: the
+ * same key set rule (openi.cn "VDN-MiniMax-H3", technical principles) read
+ * from the keys' side, with keys grouped by the query rows that see them
+ * (frame blocks by index with their
  * non-anchor frames, skipped when empty; then the anchor-frame and text keys,
  * skipped when empty):
  *   key_intervals   [capacity][VDN_MAX_KEY_INTERVALS][2] int64: the group's
@@ -348,7 +373,8 @@ int vdn_local_attn_key_blocks(int F, int tokens_per_frame, int n_text,
 
 /* Query rows per tile used by the forward kernel for a head_dim / dtype pair
  * (so callers can reproduce its schedule with vdn_local_attn_tile_schedule),
- * or a negative vdn_status_t. */
+ * or a negative vdn_status_t.  An implementation parameter: no passage of
+ * the pages defines it. */
 int vdn_local_attn_kernel_tile_m(int head_dim, int dtype);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until
