@@ -97,14 +97,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
     return st == 0 ? Vs0 : st == 1 ? Vs1 : st == 2 ? Vs2 : Vs3;
   };
 
+  __shared__ int s_next;  // the next tile's slot, handed from wave 0 to the others
+
+  // One query tile, given its slot in the XCD queues (slot w: queue w % 8,
+  // position w / 8); `claim` is the pending claim on the next one.
+  auto run_tile = [&](const int wslot, PendingClaim& claim) __attribute__((always_inline)) {
   // ---- which tile (XCD-aware, the last tiles of each XCD in halves)
-  const TileSlot slot = tile_slot(blockIdx.x, p.per_xcd, p.split_tail);
+  const TileSlot slot = tile_slot(wslot, p.per_xcd, p.split_tail);
   const int t = slot.tile;
   if (t >= p.total_tiles) return;
-  const int bh = t / p.tiles_per_bh;
-  const int rank = undeal(t - bh * p.tiles_per_bh, p.tiles_per_bh, p.deal);
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
+  // (divisors opaque per tile: their reciprocals are then formed here, not
+  // hoisted out of the tile loop and held in registers across every step)
+  int tpb = p.tiles_per_bh, deal = p.deal, nh = p.H;
+  asm volatile("" : "+s"(tpb), "+s"(deal), "+s"(nh));
+  const int bh = t / tpb;
+  const int rank = undeal(t - bh * tpb, tpb, deal);
+  const int b = bh / nh;
+  const int h = bh - b * nh;
   int bi = 0;
   while (bi + 1 < p.n_qblocks && p.blk[bi + 1].tile_prefix <= rank) ++bi;
   const KeyList kl = load_key_list(p.blk[bi]);
@@ -345,6 +354,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
   auto body = [&](int step, auto stage_c) {
     constexpr int st = decltype(stage_c)::value;
     issue_step(step + NS - 1, IC<(st + NS - 1) % NS>{});
+    // the claim on the next tile goes out with this tile's last step (tiles
+    // are then handed out in the order workgroups finish; the end-of-step
+    // wait covers the atomic)
+    if (step + 1 >= nsteps) claim.issue(p.queue, tid);
     if (active) compute(step, stage_c);
     sync_step();
   };
@@ -397,6 +410,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
       p.lse[(int64_t(b) * p.H + h) * p.S + row] = (m_run - kFp8PShift + __log2f(l_tot)) * kLn2;
     }
   }
+  };  // run_tile
+
+  // Each workgroup starts on its own slot; persistent (p.queue set), it then
+  // claims slots of its home queue (block index % 8) and, once that is
+  // empty, of the other XCDs' queues.  Otherwise that one slot is all.
+  int wslot = blockIdx.x;
+  int steal = 1;  // next queue to try once the home queue is empty
+  for (;;) {
+    PendingClaim claim;
+    run_tile(wslot, claim);
+    if (p.queue == nullptr) break;
+    if (threadIdx.x == 0) s_next = next_slot(p.queue, claim, p.per_xcd + p.split_tail, p.queue_wg, steal);
+    lds_barrier();
+    wslot = __builtin_amdgcn_readfirstlane(s_next);
+    lds_barrier();  // every wave has read the slot before wave 0 writes the next one
+    if (wslot < 0) break;
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -413,15 +443,28 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
 #define VDN_FP8_KPF 4
 #endif
 
-int launch_fwd_fp8(const FwdParams& p, int head_dim, void* stream) {
+int launch_fwd_fp8(const FwdParams& p_in, int head_dim, void* stream) {
   constexpr int kWaves = 8;
   constexpr int kStages = VDN_FP8_STAGES;
   constexpr int kKeysPerStep = VDN_FP8_KT;
   constexpr int kReadAhead = VDN_FP8_KPF;
-  const dim3 grid(unsigned(p.per_xcd + p.split_tail) * 8u);
-  const dim3 block(64 * kWaves);
   if (head_dim != 128) return int(hipErrorInvalidValue);
-  hipLaunchKernelGGL((fwd_fp8_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead>), grid, block, 0, static_cast<hipStream_t>(stream), p);
+  const auto kernel = fwd_fp8_kernel<128, kWaves, kStages, kKeysPerStep, kReadAhead>;
+  FwdParams p = p_in;
+  p.queue = nullptr;
+  p.queue_wg = 0;
+  const int slots = p.per_xcd + p.split_tail;  // per XCD queue
+  int wg = 0;
+  int* queue = nullptr;
+  const int rc = queue_for(reinterpret_cast<const void*>(kernel), kQueueFp8, &wg, &queue);
+  if (rc != 0) return rc;
+  dim3 grid(unsigned(slots) * 8u);
+  if (queue != nullptr && wg < slots) {
+    p.queue = queue;
+    p.queue_wg = wg;
+    grid = dim3(unsigned(wg) * 8u);
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * kWaves), 0, static_cast<hipStream_t>(stream), p);
   return int(hipGetLastError());
 }
 

@@ -684,17 +684,18 @@ __device__ int fwd_queues[kQueueSlots * kQueueInts];
 // workgroups per XCD that fill the device (0: not persistent).
 struct QueueDevice {
   int* base = nullptr;
-  int wg[2] = {-1, -1};  // [head_dim 64 / 128]
+  int wg[kQueueKernels] = {-1, -1, -1};
 };
 std::mutex g_queue_mu;
 QueueDevice g_queue_dev[kMaxScratchDevices];
 std::atomic<unsigned> g_queue_seq{0};
+}  // namespace
 
 // The counter set and workgroups per XCD for one launch of `kernel` (one
 // resident workgroup per CU as its resources allow, the CUs split evenly
 // over the 8 XCDs), or queue = nullptr for a launch of one workgroup per
-// slot.
-int queue_for(const void* kernel, int dim_i, int* wg_per_xcd, int** queue) {
+// slot.  `kind` < kQueueKernels names the kernel instance.
+int queue_for(const void* kernel, int kind, int* wg_per_xcd, int** queue) {
   *queue = nullptr;
   *wg_per_xcd = 0;
   int dev = 0;
@@ -709,7 +710,7 @@ int queue_for(const void* kernel, int dim_i, int* wg_per_xcd, int** queue) {
     if (e != hipSuccess) return int(e);
     qd.base = static_cast<int*>(addr);
   }
-  int& wg = qd.wg[dim_i];
+  int& wg = qd.wg[kind];
   if (wg < 0) {
     int cus = 0, per_cu = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -723,6 +724,8 @@ int queue_for(const void* kernel, int dim_i, int* wg_per_xcd, int** queue) {
   return 0;
 }
 
+namespace {
+
 template <int D, bool FUSE>
 int launch_bf16(const FwdParams& p_in, hipStream_t st) {
   constexpr int NS = FUSE ? 2 : kStages;
@@ -734,7 +737,7 @@ int launch_bf16(const FwdParams& p_in, hipStream_t st) {
   int wg = 0;
   int* queue = nullptr;
   if constexpr (!FUSE) {
-    const int rc = queue_for(reinterpret_cast<const void*>(kernel), D == 128, &wg, &queue);
+    const int rc = queue_for(reinterpret_cast<const void*>(kernel), D == 128 ? kQueueBf16D128 : kQueueBf16D64, &wg, &queue);
     if (rc != 0) return rc;
   }
   dim3 grid(unsigned(slots) * 8u);

@@ -54,7 +54,7 @@ struct FwdParams {
   const float* gate_lin;   // [B,S,H] linear-branch gate logits
   const float* lin_w;      // [H*D] RMSNorm weight
   float lin_eps;
-  // Persistent launch (bf16 kernel; nullptr: one workgroup per slot): this
+  // Persistent launch (nullptr: one workgroup per slot): this
   // launch's claim counters, kQueueInts ints (one per XCD queue, then the
   // count of finished workgroups), zero at the start and reset to zero by
   // the last workgroup; queue_wg workgroups per XCD start on slots 0 ..
@@ -143,6 +143,12 @@ int launch_fwd(const FwdParams& p, int head_dim, int dtype, void* stream);
 // set is reused only after kQueueSlots further launches in this process).
 constexpr int kQueueInts = 16;
 constexpr int kQueueSlots = 4096;
+// Kernel instances that run persistent (a cache index each).
+constexpr int kQueueBf16D64 = 0, kQueueBf16D128 = 1, kQueueFp8 = 2, kQueueKernels = 3;
+// The counter set and resident workgroups per XCD for one persistent launch
+// of `kernel` on the current device (queue = nullptr: launch one workgroup
+// per slot instead).
+int queue_for(const void* kernel, int kind, int* wg_per_xcd, int** queue);
 
 // fp8 (e4m3) variant, head_dim 128 only.
 int launch_fwd_fp8(const FwdParams& p, int head_dim, void* stream);

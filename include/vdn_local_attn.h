@@ -97,7 +97,7 @@ typedef enum {
  * each other.  Arguments are validated before any HIP call; a launch failure
  * returns VDN_ERR_HIP.
  *
- * Shared state: the bf16 kernel runs one resident workgroup per compute
+ * Shared state: the forward kernels run one resident workgroup per compute
  * unit, each taking query tiles from per-XCD work queues.  Their claim
  * counters live in the library's static device memory (no allocation), one
  * set per launch handed out in rotation from 4096 sets per device and
