@@ -78,6 +78,42 @@ def test_outliers_and_scale():
     _log("outliers", compare(out.cpu().double().numpy(), lse.cpu().double().numpy(), orf, lrf))
 
 
+# ------------------------------------ fixed reference point of the bf16 rows
+
+# Rows of query block 1 (frames 3-5 of a 12-frame, 3-frame-block video) whose
+# key list starts with frame 0: its first 128-key step sets each row's
+# reference point.  A key of frame 7 (token 700, step 5) then gets a score far
+# above that step's maximum: `q0 * k0 / sqrt(128)` nats through channel 0.
+FIXREF_CASES = {
+    # spike key channel 0; expected excess over the first step's maximum
+    "overflow": 40.0,   # ~200 log2 units: fp32 overflows unless the tile reruns
+    "rerun": 24.0,      # ~120: row sum far above 2^32 -> rerun, no overflow
+    "near": 9.75,       # ~36-41: weights up to ~2^25, no rerun
+    "in_first_step": None,  # the spike in the first step: later weights tiny
+}
+
+
+@pytest.mark.parametrize("case", list(FIXREF_CASES))
+def test_fixed_reference_point(case):
+    """The bf16 kernel fixes each row's reference point at its first step's
+    maximum + 16 and reruns a tile under the online maximum when a row sum
+    passes 2^32; every case must match the oracle (exact softmax)."""
+    w = synth.random_workload(seed=77, B=1, H=2, D=128, F=12, T=96, N=16, Bf=3, gate=True)
+    inp = synth.make_inputs(w)
+    q, k = inp["q"].clone(), inp["k"].clone()
+    rows = np.arange(3 * w.T, 6 * w.T)  # query block 1
+    q[0, rows[0]:rows[-1] + 1, 0, 0] = 40.0
+    spike = 700 if FIXREF_CASES[case] is not None else 100
+    k[0, spike, 0, 0] = FIXREF_CASES[case] if FIXREF_CASES[case] is not None else 40.0
+    inp = dict(inp, q=q, k=k)
+    og, lg = run_gpu(inp, w)
+    orf, lrf = oracle.attend(*oracle_inputs(inp), w.F, w.T, w.N, w.Bf)
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    # head 0 rows of block 1 are dominated by the spike key; the rest of the
+    # output must be untouched by the rerun
+    _log(f"fixref {case}", compare(og, lg, orf, lrf, lse_tol=BF16_LSE_BOUND))
+
+
 # ------------------------------------------- full-size workloads, sampled
 
 @pytest.mark.parametrize("name", ["medium", "768p", "768p-h4", "long"])
