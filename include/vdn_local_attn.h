@@ -104,7 +104,9 @@ typedef enum {
  * process, and each launch leaves its set zero when it ends.  So at most 4096
  * forward launches may be in flight at once per device and process, and a
  * launch recorded into a HIP graph must not run concurrently with another
- * replay of itself (replays in stream order are fine).
+ * replay of itself (replays in stream order are fine).  The first call on a
+ * device looks up the counters' address and the kernel's occupancy (host
+ * queries, cached); make it outside stream capture.
  */
 int vdn_local_attn_fwd(const void* q, const void* k, const void* v,
                        const float* gate, void* out,

@@ -241,6 +241,65 @@ def test_deterministic_and_stream():
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
+def _medium_on_gpu():
+    # the medium shape runs persistent: 130 tile slots per XCD queue, more
+    # than the 32 resident workgroups of an XCD
+    w = synth.WORKLOADS["medium"]
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    return w, q, k, v, inp["gate"].to(dev)
+
+
+def test_persistent_launches_on_concurrent_streams():
+    """Forward launches in flight together on three streams each take their
+    own set of claim counters: every one matches a launch run alone, bit for
+    bit (a shared set would skip or repeat tiles)."""
+    w, q, k, v, gate = _medium_on_gpu()
+    ref = torch.full_like(q, float("nan"))
+    B.vdn_local_attn_fwd(q, k, v, gate, ref, w.F, w.T, w.N, w.Bf)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    outs = [torch.full_like(q, float("nan")) for _ in streams]
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for st, o in zip(streams, outs):
+            with torch.cuda.stream(st):
+                B.vdn_local_attn_fwd(q, k, v, gate, o, w.F, w.T, w.N, w.Bf, stream=st.cuda_stream)
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.equal(o, ref)
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+
+
+def test_persistent_launch_replayed_from_a_graph():
+    """A forward launch recorded into a HIP graph keeps its counter set; each
+    launch leaves the set zero, so replays in stream order, with eager
+    launches and other work between them, all match the eager result."""
+    w, q, k, v, gate = _medium_on_gpu()
+    ref = torch.full_like(q, float("nan"))
+    B.vdn_local_attn_fwd(q, k, v, gate, ref, w.F, w.T, w.N, w.Bf)  # first call: outside capture
+    torch.cuda.synchronize()
+    out = torch.full_like(q, float("nan"))
+    eager = torch.full_like(q, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=side):
+        B.vdn_local_attn_fwd(q, k, v, gate, out, w.F, w.T, w.N, w.Bf, stream=side.cuda_stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        eager.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        B.vdn_local_attn_fwd(q, k, v, gate, eager, w.F, w.T, w.N, w.Bf)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        assert torch.equal(eager, ref), rep
+
+
 def test_gate_none_vs_zero_logits():
     w = synth.random_workload(seed=11, H=2, D=128, F=6, T=64, N=16, Bf=2)
     inp = synth.make_inputs(w)
