@@ -35,6 +35,7 @@
 #include <atomic>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "fwd_common.hpp"
 
@@ -150,6 +151,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int lr = lane & 31;
   const int hh = lane >> 5;
+  // A half tile (128 rows) runs on all 8 waves with the keys of every step
+  // split between two: waves w and w+4 take the same 32 rows, key blocks
+  // 0-1 and 2-3 of each step, and merge their partial rows at the end.  Not
+  // in the fused instance, nor for a key list of one step of at most KT/2
+  // keys (the second half of its only step would hold no key).
+  const bool ksplit = !FUSE && slot.half != 0 && n_keys > KT / 2;
+  const int rwave = ksplit ? (wave & 3) : wave;  // which 32 rows of the tile
+  const int kbo = ksplit ? (NKB / 2) * (wave >> 2) : 0;  // first key block of the step
 
   const int64_t rs = int64_t(p.H) * D;  // token stride (elements)
   const int64_t rsb = rs * 2;           // token stride (bytes)
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // ---- Q rows for this wave, kept in registers as MFMA B operands.
   bf16x8 qreg[NDS];
   {
-    const int lrow = wave * QW + lr;
+    const int lrow = rwave * QW + lr;
     const __bf16* src = qg + int64_t(row0 + lrow) * rs + hh * 8;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 
   // a wave whose rows all lie past the end of the query block (the last
   // tile of a block) only helps with the DMA and the barriers
-  const bool active = __builtin_amdgcn_readfirstlane(wave) * 32 < rows;
+  const bool active = rwave * 32 < rows;
   const float c = p.score_scale_log2;
   const int nsteps = (n_keys + KT - 1) / KT;
   [[maybe_unused]] const bf16x2 kOnes2 = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
@@ -278,22 +287,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // S^T = K Q^T for the KT keys in K stage `stage_c`.  The K fragments run
   // KPF reads ahead of the MFMAs that consume them (a read issued just
   // before its MFMA leaves the LDS latency on the critical path).
-  auto qk = [&](const char* ks, f32x16 (&s)[NKB]) {
-    constexpr int NF = NDS * NKB;  // fragments (= MFMAs) per step
+  auto qk = [&](const char* ks, auto& s) {
+    constexpr int NK = std::extent<std::remove_reference_t<decltype(s)>>::value;  // key blocks
+    constexpr int NF = NDS * NK;  // fragments (= MFMAs) per step
     constexpr int PF = KPF < NF ? KPF : NF;
-    // fragment f: key block f % NKB, k-step f / NKB (the NKB accumulators
+    // fragment f: key block f % NK, k-step f / NK (the NK accumulators
     // rotate, so consecutive MFMAs never share one)
     auto frag = [&](int f) {
-      return *reinterpret_cast<const bf16x8*>(ks + (f % NKB) * 32 * RB + k_roff(f / NKB));
+      return *reinterpret_cast<const bf16x8*>(ks + (f % NK) * 32 * RB + k_roff(f / NK));
     };
     bf16x8 fr[PF];
 #pragma unroll
     for (int f = 0; f < PF; ++f) fr[f] = frag(f);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int kb = 0; kb < NK; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      s[f % NKB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % PF], qreg[f / NKB], s[f % NKB], 0, 0, 0);
+      s[f % NK] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[f % PF], qreg[f / NK], s[f % NK], 0, 0, 0);
       if (f + PF < NF) fr[f % PF] = frag(f + PF);
 #if VDN_PIN_QK
       // keep this order: the scheduler would otherwise pull the reads back
@@ -305,8 +315,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 
   // O^T += V^T P^T for the KT keys in V stage `stage_c` (V^T fragments by
   // transposing LDS reads).
-  auto pv = [&](const char* vs, const bf16x8 (&pk)[NKB][2]) {
-    constexpr int NF = NKB * 2 * NDB;  // fragments (= MFMAs) per step: (kb, half, db)
+  auto pv = [&](const char* vs, const auto& pk) {
+    constexpr int NK = std::extent<std::remove_reference_t<decltype(pk)>>::value;  // key blocks
+    constexpr int NF = NK * 2 * NDB;  // fragments (= MFMAs) per step: (kb, half, db)
     constexpr int PF = VPF < NF ? VPF : NF;
     auto frag = [&](int f) {
       const int db = f % NDB, kh = f / NDB;  // kh = 2 kb + half
@@ -327,13 +338,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   };
 
   // Row maximum of a step's scores (both halves of the wave), in log2 units.
-  auto row_max = [&](const f32x16 (&s)[NKB]) {
+  auto row_max = [&](const auto& s) {
+    constexpr int NK = std::extent<std::remove_reference_t<decltype(s)>>::value;
     // one running maximum per key block, each step folding two scores with
     // a three-input max (the compiler's own form takes a two-input max per
     // pair and a three-input max per two pairs: 3 ops per 4 scores, not 2)
-    float mb[NKB];
+    float mb[NK];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NK; ++kb) {
       mb[kb] = fmaxf(s[kb][0], s[kb][1]);
 #pragma unroll
       for (int r = 2; r < 16; r += 2)
@@ -341,7 +353,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     }
     float mx = mb[0];
 #pragma unroll
-    for (int kb = 1; kb < NKB; ++kb) mx = fmaxf(mx, mb[kb]);
+    for (int kb = 1; kb < NK; ++kb) mx = fmaxf(mx, mb[kb]);
     return xhalf_max(mx) * c;
   };
   // Raise the running maximum only when the step's maximum exceeds it by
@@ -362,11 +374,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // the fp32 weights (two partial sums per lane): the bf16 dot-product form
   // over the rounded weights issues on the matrix pipe's side of the SIMD
   // and stalls the MFMAs running beside it, while fp32 adds co-issue.
-  auto exp_pack = [&](const f32x16 (&s)[NKB], bf16x8 (&pk)[NKB][2]) {
+  auto exp_pack = [&](const auto& s, auto& pk) {
+    constexpr int NK = std::extent<std::remove_reference_t<decltype(s)>>::value;
     const float mneg = -m_run;
     float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int kb = 0; kb < NK; ++kb) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         bf16x8 v8;
@@ -420,9 +433,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // `tail` (compile-time) allows a partial step (masked past the end of the
   // key list).
   constexpr int kOnline = 0, kFirst = 1, kFixed = 2;
-  auto body = [&](int step, auto stage_c, auto last_c, auto kind_c, auto tail_c) __attribute__((always_inline)) {
+  // `ks_c` (compile-time) selects the key-split half tile: this wave's half of
+  // every step's key blocks.
+  auto body = [&](int step, auto stage_c, auto last_c, auto kind_c, auto tail_c, auto ks_c) __attribute__((always_inline)) {
     constexpr int st = decltype(stage_c)::value;
     constexpr int kind = decltype(kind_c)::value;
+    constexpr bool KS = decltype(ks_c)::value != 0;
+    constexpr int NK = KS ? NKB / 2 : NKB;  // key blocks of the step this wave scores
     if constexpr (decltype(last_c)::value != 0) {
       issue_lin(lin_stage(IC<(st + NS - 1) % NS>{}));
     } else {
@@ -435,20 +452,21 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     // workgroups finish, and the end-of-step wait covers the atomic.
     if constexpr (!FUSE && decltype(tail_c)::value != 0) claim.issue(p.queue, tid);
     if (active) {
-      f32x16 s[NKB];
-      qk(kstage(stage_c), s);
+      const int kofs = KS ? kbo * 32 * RB : 0;  // bytes to the wave's first key block
+      f32x16 s[NK];
+      qk(kstage(stage_c) + kofs, s);
       if constexpr (decltype(tail_c)::value != 0) {
-        const int j0 = step * KT;
-        if (j0 + KT > n_keys) mask_tail<NKB>(s, n_keys - j0, hh);
+        const int j0 = step * KT + (KS ? 32 * kbo : 0);
+        if (step * KT + KT > n_keys) mask_tail<NK>(s, n_keys - j0, hh);
       }
       if constexpr (kind == kOnline) {
         rescale(row_max(s));
       } else if constexpr (kind == kFirst) {
         m_run = row_max(s) + kRefHeadroom;
       }
-      bf16x8 pk[NKB][2];
+      bf16x8 pk[NK][2];
       exp_pack(s, pk);
-      pv(vstage(stage_c), pk);
+      pv(vstage(stage_c) + kofs, pk);
     }
     // the next step reads K and V of step+1: batches step+2 .. step+NS-1
     // may still be in flight
@@ -469,18 +487,18 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     lds_barrier();
   };
   // The whole key list with the online maximum.
-  auto run_online = [&]() __attribute__((always_inline)) {
+  auto run_online = [&](auto ks_c) __attribute__((always_inline)) {
     prologue();
     if constexpr (!FUSE) {
       for (int step = 0;;) {
-        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{}, ks_c);
         if (++step >= nsteps) break;
-        body(step, IC<1 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+        body(step, IC<1 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{}, ks_c);
         if (++step >= nsteps) break;
         if constexpr (NS > 2) {
-          body(step, IC<2 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+          body(step, IC<2 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{}, ks_c);
           if (++step >= nsteps) break;
-          body(step, IC<3 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+          body(step, IC<3 % NS>{}, IC<0>{}, IC<kOnline>{}, IC<1>{}, ks_c);
           if (++step >= nsteps) break;
         }
       }
@@ -488,14 +506,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       // the same loop with the last step (nsteps >= 1) taken out of it
       int step = 0;
       for (; step + 2 < nsteps; step += 2) {
-        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
-        body(step + 1, IC<1>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
+        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{}, ks_c);
+        body(step + 1, IC<1>{}, IC<0>{}, IC<kOnline>{}, IC<1>{}, ks_c);
       }
       if (step + 2 == nsteps) {
-        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{});
-        body(step + 1, IC<1>{}, IC<1>{}, IC<kOnline>{}, IC<1>{});
+        body(step, IC<0>{}, IC<0>{}, IC<kOnline>{}, IC<1>{}, ks_c);
+        body(step + 1, IC<1>{}, IC<1>{}, IC<kOnline>{}, IC<1>{}, ks_c);
       } else {
-        body(step, IC<0>{}, IC<1>{}, IC<kOnline>{}, IC<1>{});
+        body(step, IC<0>{}, IC<1>{}, IC<kOnline>{}, IC<1>{}, ks_c);
       }
     }
   };
@@ -508,7 +526,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   // fp32 range) sends the workgroup through the key list again.
   auto vote_redo = [&]() __attribute__((always_inline)) {
     const float l_chk = xhalf_sum(l_run);
-    const bool bad = wave * QW + lr < rows && !(l_chk <= 0x1p32f);
+    const bool bad = rwave * QW + lr < rows && !(l_chk <= 0x1p32f);
     if (tid == 0) redo = 0;
     lds_barrier();
     if (__any(bad) && lane == 0) redo = 1;
@@ -522,36 +540,71 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   };
+  auto run_keys = [&](auto ks_c) __attribute__((always_inline)) {
   if constexpr (FIXREF) {
     // step 0 sets the reference point (peeled); only the last step can be
     // partial (peeled; fused, it fetches the linear rows); a rerun takes the
     // online maximum
     prologue();
     if (nsteps == 1) {
-      body(0, IC<0>{}, IC<FUSE ? 1 : 0>{}, IC<kFirst>{}, IC<1>{});
+      body(0, IC<0>{}, IC<FUSE ? 1 : 0>{}, IC<kFirst>{}, IC<1>{}, ks_c);
     } else {
-      body(0, IC<0>{}, IC<0>{}, IC<kFirst>{}, IC<0>{});
+      body(0, IC<0>{}, IC<0>{}, IC<kFirst>{}, IC<0>{}, ks_c);
       int step = 1;
       for (; step + 2 < nsteps; step += 2) {
-        body(step, IC<1>{}, IC<0>{}, IC<kFixed>{}, IC<0>{});
-        body(step + 1, IC<0>{}, IC<0>{}, IC<kFixed>{}, IC<0>{});
+        body(step, IC<1>{}, IC<0>{}, IC<kFixed>{}, IC<0>{}, ks_c);
+        body(step + 1, IC<0>{}, IC<0>{}, IC<kFixed>{}, IC<0>{}, ks_c);
       }
       if (step + 2 == nsteps) {
-        body(step, IC<1>{}, IC<0>{}, IC<kFixed>{}, IC<0>{});
-        body(step + 1, IC<0>{}, IC<FUSE ? 1 : 0>{}, IC<kFixed>{}, IC<1>{});
+        body(step, IC<1>{}, IC<0>{}, IC<kFixed>{}, IC<0>{}, ks_c);
+        body(step + 1, IC<0>{}, IC<FUSE ? 1 : 0>{}, IC<kFixed>{}, IC<1>{}, ks_c);
       } else {
-        body(step, IC<1>{}, IC<FUSE ? 1 : 0>{}, IC<kFixed>{}, IC<1>{});
+        body(step, IC<1>{}, IC<FUSE ? 1 : 0>{}, IC<kFixed>{}, IC<1>{}, ks_c);
       }
     }
     if (vote_redo()) {
       m_run = -__builtin_inff();
       reset();
-      run_online();
+      run_online(ks_c);
     }
   } else {
-    run_online();
+    run_online(ks_c);
   }
+  };
+  if (ksplit)
+    run_keys(IC<1>{});
+  else
+    run_keys(IC<0>{});
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no DMA outlives the workgroup
+  if (ksplit) {
+    // Waves 4-7 hand their partial rows (accumulator, reference point, row
+    // sum, in the same lane layout) to the wave with the same rows, through
+    // the ring, which every wave has finished reading and whose last DMA
+    // has landed once all have passed the barrier.
+    lds_barrier();
+    float* xacc = reinterpret_cast<float*>((wave & 2) ? Ks1 : Ks0) + (wave & 1) * (NDB * 16 * 64);
+    float* xml = reinterpret_cast<float*>(Vs0) + (wave & 3) * 128;
+    if (wave >= 4) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xacc[(db * 16 + r) * 64 + lane] = acc[db][r];
+      xml[lane] = m_run;
+      xml[64 + lane] = l_run;
+    }
+    lds_barrier();
+    if (wave < 4) {
+      const float mp = xml[lane], lp = xml[64 + lane];
+      const float mn = fmaxf(m_run, mp);
+      const float aw = __builtin_amdgcn_exp2f(m_run - mn), ap = __builtin_amdgcn_exp2f(mp - mn);
+      l_run = l_run * aw + lp * ap;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = acc[db][r] * aw + xacc[(db * 16 + r) * 64 + lane] * ap;
+      m_run = mn;
+    }
+  }
 
   // ---- epilogue: normalise, gate, store bf16, optional log-sum-exp
   // (lane-derived offsets re-formed here from an opaque thread index, so
@@ -562,7 +615,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
   __bf16* og = static_cast<__bf16*>(p.out) + bh_off;
   const int lrow = wave * QW + lr_e;
   const float l_tot = xhalf_sum(l_run);
-  if (lrow < rows) {
+  if (lrow < rows && !(ksplit && wave >= 4)) {
     const int row = row0 + lrow;
     float scale = 1.0f / l_tot;
     if (p.gate != nullptr) {
