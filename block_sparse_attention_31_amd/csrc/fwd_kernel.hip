@@ -9,11 +9,22 @@
 // ("Gated Fusion Mechanism" on the same page).
 //
 // Work decomposition
-//   One workgroup = NW waves = one tile of 32*NW query rows of one (sample,
-//   head, query block); each wave owns 32 query rows.  The key list of the
-//   block is the virtual concatenation of <= 3 token intervals, walked in
-//   steps of KT keys; only the last step can be partial.  Default shape: 8
-//   waves (two per SIMD), 128 keys per step, a 2-stage LDS ring.
+//   A tile is 32*NW query rows of one (sample, head, query block); each wave
+//   owns 32 of them.  The key list of the block is the virtual concatenation
+//   of <= 3 token intervals, walked in steps of KT keys; only the last step
+//   can be partial.  Default shape: 8 waves (two per SIMD), 128 keys per
+//   step, a 2-stage LDS ring.  The launch is persistent: one resident
+//   workgroup per CU takes tiles from its XCD's queue and, once that is
+//   empty, from the other XCDs' (one atomic claim per tile).  A half tile
+//   (128 rows, at the end of a queue) runs on all 8 waves with each step's
+//   key blocks split between waves w and w+4, which merge their rows at the
+//   end.
+//
+// Softmax
+//   Each row's weights are exponentiated against a reference point fixed at
+//   its first step's maximum + 16 (log2 units): no per-step maximum and no
+//   rescale.  A row whose sum would pass 2^32 sends its workgroup through the
+//   key list again under the online maximum.
 //
 // Matrix layout on the MFMA units (v_mfma_f32_32x32x16_bf16)
 //   S^T = K Q^T: A = K rows from LDS, B = Q rows held in registers.  The
