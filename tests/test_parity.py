@@ -129,6 +129,20 @@ def test_workload_sampled(name):
     assert np.isfinite(og).all()
 
 
+def test_head_dim_64_persistent_sampled():
+    """head_dim 64 at the medium geometry: 16 heads x 65 tiles, 130 slots per
+    XCD queue, so the persistent launch with stealing runs the D = 64
+    instance; sampled rows of three heads against the oracle."""
+    w = synth.random_workload(seed=64, B=1, H=16, D=64, F=16, T=1024, N=128, Bf=5, gate=True)
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w)
+    rows = sample_rows(w, _tile_m(w), n_random=6, seed=6)
+    heads = [0, 7, 15]
+    orf, lrf = oracle.attend(*oracle_inputs(subset_heads(inp, heads)), w.F, w.T, w.N, w.Bf, rows=rows)
+    _log("d64 persistent", compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows))
+    assert np.isfinite(og).all()
+
+
 def test_medium_four_heads_dealt_full():
     """Four heads of the medium shape: 33 tiles per XCD share, so each head's
     tile list is dealt over two shares and the last 16 tiles of every share
