@@ -170,6 +170,23 @@ def test_long_video_sampled():
           [ref[0][sel], None, None, ref[3][sel]])
 
 
+def test_long_video_one_head_full():
+    # the long-video launch (2 samples x 32 heads, 42 frames, S = 42848): every
+    # gradient of head 17 of the second sample compared element by element,
+    # including dk and dv of the two-frame last block, its key groups and the
+    # anchor/text group, which the sampled test above leaves out
+    w = synth.WORKLOADS["long"]
+    inp = synth.make_inputs(w)
+    dout = synth.make_dout(w)
+    got = run_bwd(inp, dout, w)
+    b, h = 1, 17
+    sub = {n: inp[n][b:b + 1, :, h:h + 1].contiguous() for n in ("q", "k", "v", "gate")}
+    sub["scales"] = None
+    ref = _oracle(sub, dout[b:b + 1, :, h:h + 1].contiguous(), w)
+    check("long sample 1 head 17 (all gradients)",
+          [None if t is None else t[b:b + 1, :, h:h + 1] for t in got], ref)
+
+
 def test_768p_sampled():
     # full 768p size: dq and dgate of sampled rows (every block edge, both
     # sides of every 256-row dQ tile boundary, random rows) of four heads
