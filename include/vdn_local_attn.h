@@ -347,8 +347,9 @@ int vdn_local_attn_count_pairs(int F, int tokens_per_frame, int n_text,
  * lists over (sample, head) and give each of the 8 XCDs one contiguous
  * eighth, in order; a list that spans several eighths is dealt over them
  * (entry s to the (s mod k)-th), and the last tiles of an eighth may run as
- * two halves of tile_m / 2 rows (schedule only: the results do not depend
- * on it).
+ * two halves of tile_m / 2 rows (schedule only: the results agree up to
+ * rounding; the bf16 forward splits a half's keys between two waves and
+ * merges their rows, which rounds differently from one wave).
  */
 int vdn_local_attn_tile_schedule(int F, int tokens_per_frame, int n_text,
                                  int block_frames, int tile_m, int32_t* out,
