@@ -400,7 +400,8 @@ def test_fp8_four_heads_sampled():
     (measured relative L2 0.015, against 0.008-0.009 on three heads of the
     32-head launch: there 28% of sampled rows have fewer than 50 effective
     keys, here 5%, and a row that one key dominates has large outputs that
-    come out nearly exact, its largest weight being exact in e4m3)."""
+    come out nearly exact: the rounding of its dominant weight cancels
+    against the row sum of the same rounded weights)."""
     import dataclasses
     w = dataclasses.replace(synth.WORKLOADS["768p-fp8"], name="768p-fp8-h4", H=4)
     inp = synth.make_inputs(w)
