@@ -171,6 +171,34 @@ def test_768p_dense_mode_sampled():
     _log("768p dense", compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows))
 
 
+def test_long_dense_mode_sampled():
+    """The long-video shape run dense (block_frames = F, one 42848-key list per
+    sample, the largest launch the bench times): sampled rows of two heads of
+    both samples against the oracle."""
+    w = synth.WORKLOADS["long"]
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w, block_frames=w.F)
+    rows = sample_rows(w, _tile_m(w), n_random=8, seed=8, block_frames=w.F)
+    heads = [5, 26]
+    orf, lrf = oracle.attend(*oracle_inputs(subset_heads(inp, heads)), w.F, w.T, w.N, w.F, rows=rows)
+    _log("long dense", compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows))
+    assert np.isfinite(og).all()
+
+
+def test_fp8_768p_dense_mode_sampled():
+    """fp8 run dense (block_frames = F), as the bench's fp8 sparse-vs-dense
+    figure times it: sampled rows of two heads against the oracle."""
+    w = synth.WORKLOADS["768p-fp8"]
+    inp = synth.make_inputs(w)
+    og, lg = run_gpu(inp, w, block_frames=w.F)
+    rows = sample_rows(w, _tile_m(w), n_random=8, seed=12, block_frames=w.F)
+    heads = [2, 29]
+    sub = subset_heads(inp, heads)
+    orf, lrf = oracle.attend(*oracle_inputs(sub), w.F, w.T, w.N, w.F, rows=rows)
+    _log("768p-fp8 dense", compare(og[:, :, heads], lg[:, heads], orf, lrf, rows=rows, max_abs=FP8_MAX_ABS,
+                                   rel_l2=FP8_REL_L2_768P, lse_tol=FP8_LSE_TOL, v_rms=value_channel_rms(sub)))
+
+
 # ------------------------------------------------------ structure checks
 
 @pytest.mark.parametrize("name", ["tiny", "768p", "long"])
