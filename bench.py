@@ -11,7 +11,9 @@ event before each call on the launch stream).  Extra workloads -- the medium,
 long-video and fp8 forward configurations (each with its dense run and a CPU
 oracle sample), the backward pass, the complement linear branch, the
 two-branch fusion, the whole hybrid attention output and one GPU's 4-head
-share -- are reported under "other_workloads".
+share -- are reported under "other_workloads".  For context, "library_gemm"
+times the vendor's dense bf16 GEMM on the same GPU (a practical ceiling for
+matrix-core work on the part) and gives the forward's rate as a fraction of it.
 
     python bench.py [--steps K] [--warmup W] [--workload 768p]
 """
@@ -139,6 +141,9 @@ def main() -> int:
                     help="comma-separated extra workloads reported under 'other_workloads' "
                          "(suffixes: '-bwd' the backward pass, '-linear' the linear branch, "
                          "'-fuse' the fusion, '-hybrid' softmax + linear + fusion; '' for none)")
+    ap.add_argument("--gemm", type=int, default=8192,
+                    help="size n of the vendor bf16 GEMM (n^3) timed for context after the "
+                         "workloads (0 skips it)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -338,6 +343,26 @@ def main() -> int:
                 "algorithmic_bytes": nbytes, "config": shape_config(w),
                 "roofline": hbm_roofline(nbytes, ms, load_traffic("linear", w.name, "fuse"))}
 
+    def measure_gemm(n: int, steps: int, warmup: int):
+        """Context, not this library: the vendor's dense bf16 GEMM (torch.matmul,
+        which dispatches to hipBLASLt) on n x n x n, the same GPU and the same
+        peak, as a practical ceiling for matrix-core work on this part."""
+        g = torch.Generator(device=dev).manual_seed(1)
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+
+        def step():
+            torch.matmul(a, b, out=c)
+        ms, med, _ = time_calls(step, steps, warmup)
+        tflops = 2.0 * n ** 3 / (med * 1e-3) / 1e12
+        print(f"[bench] bf16 GEMM {n}^3 (torch.matmul): {ms:.4f} ms/step (median {med:.4f}), "
+              f"{tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        return {"what": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), same GPU; context only",
+                "ms_per_step": round(ms, 4), "ms_per_call_median": round(med, 4), "steps": steps,
+                "tflops_at_median": round(tflops, 2),
+                "pct_of_mfma_peak": round(100.0 * tflops / PEAK_TFLOPS["bf16"], 2)}
+
     def measure_hybrid(name: str, steps: int, warmup: int):
         """The hybrid attention output of one layer before the output
         projections: gated softmax branch, linear branch, fusion."""
@@ -417,6 +442,10 @@ def main() -> int:
         torch.cuda.empty_cache()
     if others:
         result["other_workloads"] = others
+    if args.gemm > 0:
+        gemm = measure_gemm(args.gemm, other_steps, args.warmup)
+        gemm["forward_vs_gemm"] = round(main_rec["tflops_at_median"] / gemm["tflops_at_median"], 4)
+        result["library_gemm"] = gemm
     if "cpu_baseline" in main_rec:
         result["cpu_baseline"] = main_rec["cpu_baseline"]
     print(json.dumps(result), flush=True)
