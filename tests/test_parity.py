@@ -51,6 +51,8 @@ RANDOM_SHAPES = [
     (1, 2, 128, 6, 100, 300, 5, True),   # text block larger than a tile
     (1, 1, 128, 5, 1, 1, 5, True),       # S = 6 (single partial tile)
     (2, 1, 64, 11, 64, 16, 11, True),    # block covers the video: dense
+    (1, 2, 64, 315, 2, 4, 5, True),      # 64 query blocks: the descriptor array full
+    (1, 1, 128, 63, 8, 4, 1, False),     # 64 query blocks of one frame each
 ]
 
 

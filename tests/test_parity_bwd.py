@@ -97,6 +97,7 @@ BWD_SHAPES = [
     (1, 1, 128, 6, 100, 300, 5, True),   # text block larger than a tile
     (1, 1, 128, 5, 1, 1, 5, True),       # S = 6
     (1, 1, 64, 11, 64, 16, 11, True),    # dense
+    (1, 2, 64, 315, 2, 4, 5, True),      # 64 query blocks and 64 key groups: both arrays full
 ]
 
 

@@ -110,6 +110,7 @@ SHAPES = [
     (1, 1, 128, 1, 9, 0, 5),      # one frame
     (1, 2, 128, 16, 257, 7, 4),   # tiles of 512 rows within 4-frame blocks
     (2, 2, 64, 42, 8, 5, 5),      # the long-video frame structure, small frames
+    (1, 1, 64, 315, 2, 4, 5),     # 63 frame blocks
 ]
 
 
