@@ -281,9 +281,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
   // with the DMA and the barriers
   const bool active = __builtin_amdgcn_readfirstlane(wave) * QW < rows;
 
-  auto compute = [&](int step, auto stage_c) {
+  auto compute = [&](int step, auto stage_c, auto dma_k, auto dma_v) {
     f32x16 s_cur[NKB];
     qk(stage_c, s_cur);
+    dma_k();
     const int j0 = step * KT;
     if (j0 + KT > n_keys) mask_tail<NKB>(s_cur, n_keys - j0, hh);
     {
@@ -332,6 +333,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
         }
       }
     }
+    dma_v();
     // row sums of the rounded weights, then O^T += V^T P^T
     const char* vs = vstage(stage_c);
 #pragma unroll
@@ -353,12 +355,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_fp8_kernel(const FwdParams p) 
   };
   auto body = [&](int step, auto stage_c) {
     constexpr int st = decltype(stage_c)::value;
-    issue_step(step + NS - 1, IC<(st + NS - 1) % NS>{});
+    // K of step + NS - 1 goes out once this step's QK products are issued,
+    // V once its weights are formed (waves with no rows issue both at once);
+    // issued together at the start of the step, the batch held back the QK
+    // products behind it
+    auto dma_k = [&]() __attribute__((always_inline)) { issue(step + NS - 1, IC<(st + NS - 1) % NS>{}, IC<1>{}); };
+    auto dma_v = [&]() __attribute__((always_inline)) { issue(step + NS - 1, IC<(st + NS - 1) % NS>{}, IC<0>{}); };
     // the claim on the next tile goes out with this tile's last step (tiles
     // are then handed out in the order workgroups finish; the end-of-step
     // wait covers the atomic)
     if (step + 1 >= nsteps) claim.issue(p.queue, tid);
-    if (active) compute(step, stage_c);
+    if (active) {
+      compute(step, stage_c, dma_k, dma_v);
+    } else {
+      dma_k();
+      dma_v();
+    }
     sync_step();
   };
 

@@ -451,12 +451,18 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     constexpr int kind = decltype(kind_c)::value;
     constexpr bool KS = decltype(ks_c)::value != 0;
     constexpr int NK = KS ? NKB / 2 : NKB;  // key blocks of the step this wave scores
-    if constexpr (decltype(last_c)::value != 0) {
-      issue_lin(lin_stage(IC<(st + NS - 1) % NS>{}));
-    } else {
-      issue(step + NS - 1, kstage(IC<(st + NS - 1) % NS>{}), IC<1>{});
-      issue(step + NS - 1, vstage(IC<(st + NS - 1) % NS>{}), IC<0>{});
-    }
+    constexpr bool LAST = decltype(last_c)::value != 0;
+    if constexpr (LAST) issue_lin(lin_stage(IC<(st + NS - 1) % NS>{}));
+    // K of step + NS - 1 goes out once this step's QK products are issued,
+    // V once its weights are formed (waves with no rows issue both at once).
+    // Issued together at the start of the step, the batch held back the QK
+    // products behind it.
+    auto dma_k = [&]() __attribute__((always_inline)) {
+      if constexpr (!LAST) issue(step + NS - 1, kstage(IC<(st + NS - 1) % NS>{}), IC<1>{});
+    };
+    auto dma_v = [&]() __attribute__((always_inline)) {
+      if constexpr (!LAST) issue(step + NS - 1, vstage(IC<(st + NS - 1) % NS>{}), IC<0>{});
+    };
     // The claim on the next tile goes out with the tile's last step (the one
     // that may be partial; the first such step once, so a rerun or the
     // online loop claims early): tiles are then handed out in the order their
@@ -466,6 +472,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       const int kofs = KS ? kbo * 32 * RB : 0;  // bytes to the wave's first key block
       f32x16 s[NK];
       qk(kstage(stage_c) + kofs, s);
+      dma_k();
       if constexpr (decltype(tail_c)::value != 0) {
         const int j0 = step * KT + (KS ? 32 * kbo : 0);
         if (step * KT + KT > n_keys) mask_tail<NK>(s, n_keys - j0, hh);
@@ -477,7 +484,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
       }
       bf16x8 pk[NK][2];
       exp_pack(s, pk);
+      dma_v();
       pv(vstage(stage_c) + kofs, pk);
+    } else {
+      dma_k();
+      dma_v();
     }
     // the next step reads K and V of step+1: batches step+2 .. step+NS-1
     // may still be in flight
