@@ -187,6 +187,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     for (int ds = 0; ds < NDS; ++ds)
       qreg[ds] = lrow < rows ? *reinterpret_cast<const bf16x8*>(src + ds * 16) : bf16x8{};
   }
+  // The row's gate logit, read with Q so that its load overlaps Q's.
+  float g_pre = 0.f;
+  {
+    const int lrow = rwave * QW + lr;
+    if (p.gate != nullptr && lrow < rows) g_pre = p.gate[(int64_t(b) * p.S + row0 + lrow) * p.H + h];
+  }
   // With the two-branch fusion: the row's linear-branch factor, sigmoid of
   // its gate over the token's RMS (from the per-head sums of squares), read
   // here so that its loads overlap Q's.
@@ -641,8 +647,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const FwdParams p)
     const int row = row0 + lrow;
     float scale = 1.0f / l_tot;
     if (p.gate != nullptr) {
-      const float g = p.gate[(int64_t(b) * p.S + row) * p.H + h];
-      scale *= 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
+      scale *= 1.0f / (1.0f + __builtin_amdgcn_exp2f(-g_pre * kLog2e));
     }
     __bf16* dst = og + int64_t(row) * rs;
     if constexpr (!FUSE) {
