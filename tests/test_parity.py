@@ -317,6 +317,40 @@ def test_persistent_launches_on_concurrent_streams():
         torch.cuda.synchronize()
 
 
+def test_persistent_counter_sets_reused():
+    """More launches than the library has claim-counter sets (4096, taken in
+    rotation): every set is used twice, so this passes only if each
+    persistent launch leaves its set at zero.  A stale count would skip
+    tiles (NaN left in the output) or hand one out twice.  64 heads of 20
+    frames x 64 tokens give 64 tiles per XCD queue, more than the 32 resident
+    workgroups, so every launch runs persistent; the result is also checked
+    against the oracle on two heads."""
+    w = synth.random_workload(seed=4096, B=1, H=64, D=128, F=20, T=64, N=0, Bf=5, gate=True)
+    tiles = len(B.vdn_local_attn_tile_schedule(w.F, w.T, w.N, w.Bf, _tile_m(w))) * w.H
+    assert (tiles + 7) // 8 > 32
+    inp = synth.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    gate = inp["gate"].to(dev)
+    ref = torch.full_like(q, float("nan"))
+    B.vdn_local_attn_fwd(q, k, v, gate, ref, w.F, w.T, w.N, w.Bf)
+    torch.cuda.synchronize()
+    heads = [0, w.H - 1]
+    sub = subset_heads(inp, heads)
+    orf, lrf = oracle.attend(*oracle_inputs(sub), w.F, w.T, w.N, w.Bf)
+    _log("persistent shape", compare(ref.cpu().float().numpy()[:, :, heads], None, orf, lrf))
+    out = torch.empty_like(q)
+    n_launch = 4096 + 64
+    for i in range(n_launch):
+        check = i % 512 == 0 or i >= n_launch - 3
+        if check:
+            out.fill_(float("nan"))
+        B.vdn_local_attn_fwd(q, k, v, gate, out, w.F, w.T, w.N, w.Bf)
+        if check:
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), i
+
+
 def test_persistent_launch_replayed_from_a_graph():
     """A forward launch recorded into a HIP graph keeps its counter set; each
     launch leaves the set zero, so replays in stream order, with eager
