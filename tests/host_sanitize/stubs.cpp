@@ -1,7 +1,7 @@
 // Host-only stand-ins for the HIP side of libvdn_local_attn, used to build the
 // C-ABI front end (api.cpp) and the scheduler (schedule.cpp) with g++ under
 // AddressSanitizer and UndefinedBehaviorSanitizer.  Every launcher reports
-// that no device is present; the tests that load this build only reach them
+// that no device is present; the tests that load the sanitizer build only reach them
 // through calls whose validation passes, which the CPU tests never make.
 #include <hip/hip_runtime.h>
 
